@@ -1,0 +1,143 @@
+/*
+ * kq.h — C ABI of libkq, the MI355X (gfx950) KroQuant activation quantizer.
+ *
+ * KroQuant multiplies every 32-channel block of a bf16 activation by a
+ * learned invertible 32x32 matrix T_j and quantizes the result to MXFP4
+ * (source: "KroQuant: Kronecker-Structured Block Transforms for Efficient
+ * Post-Training Quantization of Diffusion Transformers", research-map summary,
+ * sections "Problem" and "Approach"; the KroQuant abstract).  T_j is the
+ * Kronecker product of five 2x2 unit-determinant LU factors, 15 parameters per
+ * block ("Approach").  Because AdaLN/normalisation sits in front of every
+ * linear layer, this transform runs online at every denoising step (summary,
+ * "Problem"; abstract).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All buffer pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller.  The library never allocates, frees or synchronises; every call
+ *    enqueues its kernel on `stream` (a hipStream_t passed as void*, NULL for
+ *    the default stream) and returns.  Errors of the asynchronous work surface
+ *    at the caller's next synchronisation.  Calls are stateless and may be
+ *    issued from several host threads.
+ *  - Activations are row-major bf16 [tokens][ld] (element stride 1, row stride
+ *    ld elements), of which the first d channels are used; d % 32 == 0.
+ *    Channel block j is channels 32j .. 32j+31.
+ *  - Transform parameters `lu` are fp32 [d/32][5][3]: for block j and factor
+ *    b = 0..4 the triple (l, u, v) of F_b = [[1,0],[l,1]] * [[u,v],[0,1/u]];
+ *    T_j = F_4 (x) F_3 (x) F_2 (x) F_1 (x) F_0, so F_b acts on bit b of the
+ *    in-block channel index, and y = x * T_j (row vector, as X*H in LRQ-DiT
+ *    Sec. 3.2 Eq. (2)).  The Hadamard start of the summary's "Approach" is
+ *    (l,u,v) = (1, 1/sqrt2, -1/sqrt2) for every factor.
+ *  - MXFP4 output (the pages' "W4A4 MXFP4"; element and scale rules of the
+ *    OCP MX v1.0 format):
+ *      codes  uint8 [tokens][d/2]: element k of a row in the low nibble of
+ *             byte k/2 when k is even, in the high nibble when k is odd;
+ *             each nibble is an E2M1 code (sign<<3 | magnitude index,
+ *             magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *      scales uint8 [tokens][d/32]: E8M0 byte s of block j, value 2^(s-127).
+ *    s = clamp(floor(log2(amax)) - 2, -127, 127) + 127 where amax is the
+ *    largest |y| of the block (s = 0 for an all-zero block); codes are y*2^-e
+ *    rounded to nearest-even on the E2M1 grid, saturating at +-6, sign kept.
+ *    A block holding NaN or Inf gets s = 0xFF and all-zero codes.
+ *  - Arithmetic is fp32 in a fixed order (see kq_transform_quant), with fp32
+ *    denormals kept, so results are deterministic and bit-reproducible.
+ *  - Status: validation happens on the host before any HIP call, in the order
+ *    shape -> empty (tokens == 0 returns KQ_OK, launches nothing, and may pass
+ *    NULL pointers) -> NULL pointers -> alignment.  A failed launch returns
+ *    KQ_ERR_HIP.  Nothing throws across this boundary.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kq_status {
+    KQ_OK = 0,
+    KQ_ERR_NULL = 1,   /* a required pointer is NULL                         */
+    KQ_ERR_SHAPE = 2,  /* tokens < 0 or >= 2^31, d <= 0, d % 32, ld < d, ... */
+    KQ_ERR_ALIGN = 3,  /* x, codes or a stride not 16-byte aligned, ...      */
+    KQ_ERR_HIP = 4     /* the HIP runtime rejected the launch                */
+} kq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kq_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kq_version(void);
+
+/*
+ * kq_transform_quant — the online KroQuant quantizer: y = x * T_j for every
+ * (token, block), then MXFP4.  Source: summary "Approach" (Kronecker product
+ * of five 2x2 unit-determinant LU factors, 15 parameters per block, Hadamard
+ * start); abstract (invertible per-32-element block transform, then MXFP4
+ * quantization of the activations).
+ *
+ *   x       bf16 [tokens][ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= d
+ *   lu      fp32 [d/32][5][3] (4-byte aligned)
+ *   codes   uint8 [tokens][d/2], 16-byte aligned (written)
+ *   scales  uint8 [tokens][d/32] (written)
+ *
+ * Fixed fp32 order (every step one IEEE operation): per block, w_b = u_b*v_b
+ * and 1/u_b (IEEE division); for bits b = 0..4 each index pair (i, i|2^b)
+ * with bit b of i clear maps (p, q) to r = fma(l_b, q, p), s = fma(w_b, r, q);
+ * then y_k = z_k * d_k, d_k the left-to-right product over b = 0..4 of
+ * (bit b of k ? 1/u_b : u_b).  This is T = (G_4 (x)...(x) G_0)(D_4 (x)...(x) D_0)
+ * with F_b = G_b D_b, G_b = [[1,w],[l,1+l*w]], D_b = diag(u, 1/u).
+ */
+kq_status kq_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                             const float *lu, uint8_t *codes, uint8_t *scales,
+                             void *stream);
+
+/*
+ * kq_transform_f32 — the same device transform as kq_transform_quant with an
+ * fp32 store instead of the quantizer: y fp32 [tokens][d], 16-byte aligned.
+ * For checking the transform stage on its own.
+ */
+kq_status kq_transform_f32(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                           const float *lu, float *y, void *stream);
+
+/*
+ * kq_smooth_quant — per-channel scaling baseline (SmoothQuant, named as the
+ * baseline in the summary's "Key results" and in the abstract):
+ * y_c = x_c * mult_c (one fp32 multiply), then MXFP4 as above.
+ *   mult  fp32 [d], 16-byte aligned.
+ */
+kq_status kq_smooth_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          const float *mult, uint8_t *codes, uint8_t *scales,
+                          void *stream);
+
+/*
+ * kq_fwht32_quant — fixed 32-point Hadamard baseline (summary "Surprising
+ * findings" and "Experimental setup": Hadamard 32x32 block transform, FWHT):
+ * y = x * H_32 with H_32 the orthonormal Sylvester matrix of LRQ-DiT
+ * Sec. 3.2 Eq. (3), computed as five add/subtract stages over bits 0..4,
+ * (p, q) -> (p + q, p - q), then one multiply by fl32(1/sqrt(32)); then MXFP4.
+ */
+kq_status kq_fwht32_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * kq_mxfp4_quant_f32 — MXFP4 of an fp32 tensor without a transform (the
+ * quantizer stage alone).  y fp32 [tokens][ld_y], 16-byte aligned,
+ * ld_y % 4 == 0.
+ */
+kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t ld_y,
+                             uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * kq_copy_ceiling — not a quantizer: moves the same bytes as
+ * kq_transform_quant (reads the bf16 tensor, writes d/2 + d/32 bytes per row)
+ * with almost no arithmetic, to measure the achievable bandwidth of this
+ * access pattern.  Output bytes are a fold of the input, not MXFP4.
+ */
+kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          uint8_t *codes, uint8_t *scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

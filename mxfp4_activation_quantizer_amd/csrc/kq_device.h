@@ -1,0 +1,79 @@
+// kq_device.h — device-side building blocks of the gfx950 quantizer kernels.
+//
+// Everything here is written for CDNA4 (gfx950, wave64): 16-byte global
+// loads, the hardware E2M1 pack-convert with an E8M0 scale operand
+// (v_cvt_scalef32_pk_fp4_f32) and the NaN-propagating three-input maximum
+// (v_maximum3_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 -> fp32 is exact: a bf16 is the upper half of a binary32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Largest |y| over a 32-value block.  llvm.maximum propagates NaN (unlike
+// fmaxf), so a NaN anywhere in the block makes amax NaN; gfx950 issues this
+// chain as v_maximum3_f32 with |.| source modifiers, two values per op.
+__device__ __forceinline__ float block_amax(const float (&y)[32]) {
+    float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
+#pragma unroll
+    for (int k = 2; k < 32; k += 2)
+        m = __builtin_elementwise_maximum(
+            m, __builtin_elementwise_maximum(__builtin_fabsf(y[k]), __builtin_fabsf(y[k + 1])));
+    return m;
+}
+
+// E8M0 scale byte of the MXFP4 block: e = floor(log2 amax) - 2 clamped to
+// [-127, 127], stored as e + 127.  For a normal amax with biased exponent E,
+// floor(log2 amax) = E - 127, so the byte is E - 2; E < 2 (tiny, subnormal
+// or zero amax) clamps to 0; E = 255 (Inf or NaN) gives the NaN byte 0xFF.
+__device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
+    uint32_t E = (__float_as_uint(amax) >> 23) & 0xffu;
+    uint32_t s = E > 2u ? E - 2u : 0u;
+    return E == 255u ? 255u : s;
+}
+
+// Eight values -> one dword of E2M1 codes.  The gfx950 convert divides its
+// two inputs by the scale operand, whose exponent field carries the E8M0
+// byte (1.0 * 2^(s-127)), rounds to nearest even with saturation and writes
+// one byte (first input in the low nibble) into the byte lane `sel` of `old`.
+__device__ __forceinline__ uint32_t pack8_fp4(const float *y, float scale) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
+    return w;
+}
+
+// Quantize one 32-value block to 16 code bytes (4 dwords of 8 codes) and one
+// scale byte.  Non-finite blocks store all-zero codes next to the 0xFF scale.
+__device__ __forceinline__ void mxfp4_block(const float (&y)[32], u32x4 &codes,
+                                            uint32_t &sbyte) {
+    const float amax = block_amax(y);
+    const uint32_t s = e8m0_from_amax(amax);
+    const float scale = __uint_as_float(s << 23);
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = pack8_fp4(&y[8 * q], scale);
+    const bool nonfinite = (s == 255u);
+    codes = u32x4{nonfinite ? 0u : c[0], nonfinite ? 0u : c[1], nonfinite ? 0u : c[2],
+                  nonfinite ? 0u : c[3]};
+    sbyte = s;
+}
+
+}  // namespace kq

@@ -1,0 +1,433 @@
+// kq_quant.hip — gfx950 kernels of the online KroQuant quantizer and its
+// per-channel-scaling and FWHT32 baselines, plus the C ABI that launches them.
+//
+// Work decomposition.  One lane owns one unit = (token t, 32-channel block j):
+// 64 contiguous bytes of bf16 input, 16 bytes of E2M1 codes and one E8M0
+// byte of output.  Holding the whole block in one lane keeps all five
+// butterfly stages in registers with no cross-lane traffic, and makes every
+// wave-wide load/store instruction cover 64 consecutive units (4 KB of input,
+// 1 KB of codes, 64 B of scales per wave and unit-step).
+//
+// The grid is sized so that the total lane count L is a multiple of the
+// number of blocks per row nb.  Lane g then handles units g, g + L, g + 2L,
+// ... which all belong to block j = g mod nb: the per-block constants (five
+// shears and the 32-entry diagonal) are derived once per lane and stay in
+// VGPRs, and consecutive units of a lane are tstep = L / nb tokens apart.
+// Each lane issues the loads of P units before computing any of them, so
+// several 64-byte requests per lane are in flight at once.
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kq.h"
+#include "kq_device.h"
+
+namespace kq {
+
+constexpr int kBlockThreads = 256;  // 4 waves of 64 lanes
+constexpr int kUnitsInFlight = 2;   // P: units whose loads are issued together
+
+// ---------------------------------------------------------------------------
+// Sources: where a unit's 32 input values come from.
+// ---------------------------------------------------------------------------
+struct Bf16Src {
+    const uint16_t *x;
+    int64_t ld;  // row stride, elements
+    struct Raw { u32x4 v[4]; };
+    __device__ __forceinline__ void load(int t, int j, Raw &r) const {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(x + (int64_t)t * ld + (int64_t)j * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(p + i);
+    }
+    __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                z[8 * i + 2 * c] = bf16_lo(r.v[i][c]);
+                z[8 * i + 2 * c + 1] = bf16_hi(r.v[i][c]);
+            }
+    }
+};
+
+struct F32Src {
+    const float *y;
+    int64_t ld;
+    struct Raw { f32x4 v[8]; };
+    __device__ __forceinline__ void load(int t, int j, Raw &r) const {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(y + (int64_t)t * ld + (int64_t)j * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.v[i] = __builtin_nontemporal_load(p + i);
+    }
+    __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) z[4 * i + c] = r.v[i][c];
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Transform stages.
+// ---------------------------------------------------------------------------
+
+// The Kronecker-structured block transform (KroQuant summary, "Approach").
+// F_b = [[1,0],[l,1]] [[u,v],[0,1/u]] = G_b D_b with the shear pair
+// G_b = [[1,w],[l,1+l*w]], w = u*v, and D_b = diag(u, 1/u).  The Kronecker
+// mixed-product rule turns T = (x)_b F_b into (x)_b G_b times the diagonal
+// (x)_b D_b, so the kernel runs two fused multiply-adds per index pair and
+// bit, then one multiply per element by d_k = prod_b (bit b of k ? 1/u_b : u_b).
+struct KronStage {
+    const float *lu;  // [nb][5][3]
+    float l[5], w[5], dk[32];
+    __device__ __forceinline__ void setup(int j) {
+        const float *p = lu + (int64_t)j * 15;
+        float u[5], iu[5];
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            l[b] = p[3 * b + 0];
+            u[b] = p[3 * b + 1];
+            w[b] = u[b] * p[3 * b + 2];
+            iu[b] = 1.0f / u[b];  // IEEE division (correctly rounded)
+        }
+        // d_k as the running product over b = 0..4, built bit by bit.
+        dk[0] = u[0];
+        dk[1] = iu[0];
+#pragma unroll
+        for (int b = 1; b < 5; ++b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int k = 0; k < h; ++k) {
+                dk[k + h] = dk[k] * iu[b];
+                dk[k] = dk[k] * u[b];
+            }
+        }
+    }
+    __device__ __forceinline__ void apply(float (&z)[32]) const {
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h) continue;
+                const float r = __builtin_fmaf(l[b], z[i | h], z[i]);
+                const float s = __builtin_fmaf(w[b], r, z[i | h]);
+                z[i] = r;
+                z[i | h] = s;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = z[k] * dk[k];
+    }
+};
+
+// Per-channel scaling baseline: y_c = x_c * mult_c.
+struct SmoothStage {
+    const float *mult;  // [d]
+    float m[32];
+    __device__ __forceinline__ void setup(int j) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(mult + (int64_t)j * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = p[i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
+        }
+    }
+    __device__ __forceinline__ void apply(float (&z)[32]) const {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = z[k] * m[k];
+    }
+};
+
+// Orthonormal 32-point Walsh-Hadamard (Sylvester order, LRQ-DiT Eq. (3)):
+// five add/subtract stages, then one multiply by fl32(1/sqrt(32)).
+struct FwhtStage {
+    __device__ __forceinline__ void setup(int) {}
+    __device__ __forceinline__ void apply(float (&z)[32]) const {
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h) continue;
+                const float p = z[i], q = z[i | h];
+                z[i] = p + q;
+                z[i | h] = p - q;
+            }
+        }
+        const float c = 0x1.6a09e6p-3f;  // 1/sqrt(32) rounded to fp32
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = z[k] * c;
+    }
+};
+
+struct IdentityStage {
+    __device__ __forceinline__ void setup(int) {}
+    __device__ __forceinline__ void apply(float (&)[32]) const {}
+};
+
+// ---------------------------------------------------------------------------
+// Sinks: what is stored per unit.
+// ---------------------------------------------------------------------------
+struct Mxfp4Sink {
+    uint8_t *codes;   // [tokens][d/2]
+    uint8_t *scales;  // [tokens][nb]
+    int nb;
+    __device__ __forceinline__ void store(int t, int j, const float (&y)[32]) const {
+        u32x4 c;
+        uint32_t s;
+        mxfp4_block(y, c, s);
+        const int64_t unit = (int64_t)t * nb + j;
+        __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(codes) + unit);
+        scales[unit] = (uint8_t)s;
+    }
+};
+
+struct F32Sink {
+    float *y;  // [tokens][d]
+    int64_t d;
+    __device__ __forceinline__ void store(int t, int j, const float (&z)[32]) const {
+        f32x4 *p = reinterpret_cast<f32x4 *>(y + (int64_t)t * d + (int64_t)j * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = f32x4{z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]};
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The kernel template.
+// ---------------------------------------------------------------------------
+template <class Src, class Stage, class Sink, int P>
+__global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, Stage stage, Sink sink,
+                                                              int tokens, int nb, int tstep) {
+    const int g = blockIdx.x * kBlockThreads + threadIdx.x;
+    const int j = g % nb;
+    int t = g / nb;
+    if (t >= tokens) return;
+    stage.setup(j);
+    for (; t < tokens; t += P * tstep) {
+        typename Src::Raw raw[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (t + p * tstep < tokens) src.load(t + p * tstep, j, raw[p]);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int tt = t + p * tstep;
+            if (tt < tokens) {
+                float z[32];
+                Src::unpack(raw[p], z);
+                stage.apply(z);
+                sink.store(tt, j, z);
+            }
+        }
+    }
+}
+
+// Same-traffic ceiling: identical mapping and byte counts, output is an XOR
+// fold of the input instead of the quantizer.
+template <int P>
+__global__ __launch_bounds__(kBlockThreads) void copy_ceiling_kernel(Bf16Src src, uint8_t *codes,
+                                                                     uint8_t *scales, int tokens,
+                                                                     int nb, int tstep) {
+    const int g = blockIdx.x * kBlockThreads + threadIdx.x;
+    const int j = g % nb;
+    int t = g / nb;
+    for (; t < tokens; t += P * tstep) {
+        Bf16Src::Raw raw[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (t + p * tstep < tokens) src.load(t + p * tstep, j, raw[p]);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int tt = t + p * tstep;
+            if (tt < tokens) {
+                const u32x4 f = raw[p].v[0] ^ raw[p].v[1] ^ raw[p].v[2] ^ raw[p].v[3];
+                const int64_t unit = (int64_t)tt * nb + j;
+                __builtin_nontemporal_store(f, reinterpret_cast<u32x4 *>(codes) + unit);
+                scales[unit] = (uint8_t)(f[0] ^ f[1] ^ f[2] ^ f[3]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation and launch geometry.
+// ---------------------------------------------------------------------------
+static int gcd_int(int a, int b) {
+    while (b) {
+        int r = a % b;
+        a = b;
+        b = r;
+    }
+    return a;
+}
+
+struct Plan {
+    int grid;   // workgroups
+    int tstep;  // tokens between consecutive units of a lane
+};
+
+// Units per lane the grid is sized for.  KQ_UNITS_PER_LANE (read once)
+// overrides the default for launch-geometry sweeps.
+static int units_per_lane() {
+    static int cached = 0;
+    if (cached == 0) {
+        int v = 2;
+        const char *e = getenv("KQ_UNITS_PER_LANE");
+        if (e) {
+            int p = atoi(e);
+            if (p >= 1 && p <= 64) v = p;
+        }
+        cached = v;
+    }
+    return cached;
+}
+
+static bool plan_launch(int64_t tokens, int nb, Plan &pl) {
+    // The lane count must be a multiple of nb: grid a multiple of m.
+    const int64_t m = nb / gcd_int(nb, kBlockThreads);
+    const int64_t units = tokens * nb;
+    const int64_t per_wg = (int64_t)kBlockThreads * units_per_lane();
+    int64_t grid = (units + per_wg - 1) / per_wg;
+    grid = (grid + m - 1) / m * m;
+    if (grid < m) grid = m;
+    const int64_t lanes = grid * kBlockThreads;
+    if (grid > INT32_MAX / kBlockThreads) return false;
+    pl.grid = (int)grid;
+    pl.tstep = (int)(lanes / nb);
+    return true;
+}
+
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape checks common to every activation-consuming entry point.
+static kq_status check_shape(int64_t tokens, int64_t d, int64_t ld) {
+    if (tokens < 0 || tokens >= (int64_t(1) << 30)) return KQ_ERR_SHAPE;
+    if (d <= 0 || d % 32 != 0 || d > (int64_t(1) << 26)) return KQ_ERR_SHAPE;
+    if (ld < d) return KQ_ERR_SHAPE;
+    return KQ_OK;
+}
+
+template <class Kernel, class... Args>
+static kq_status launch(Kernel kernel, const Plan &pl, void *stream, Args... args) {
+    void *argv[] = {(void *)&args...};
+    hipError_t e = hipLaunchKernel((const void *)kernel, dim3(pl.grid), dim3(kBlockThreads), argv,
+                                   0, (hipStream_t)stream);
+    return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+template <class Src, class Stage, class Sink>
+static kq_status run(const Src &src, const Stage &stage, const Sink &sink, int64_t tokens, int nb,
+                     void *stream) {
+    Plan pl;
+    if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
+    return launch(block_kernel<Src, Stage, Sink, kUnitsInFlight>, pl, stream, src, stage, sink,
+                  (int)tokens, nb, pl.tstep);
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+extern "C" {
+
+const char *kq_status_str(int status) {
+    switch (status) {
+        case KQ_OK: return "KQ_OK";
+        case KQ_ERR_NULL: return "KQ_ERR_NULL: a required pointer is NULL";
+        case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE: invalid sizes or strides";
+        case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN: pointer or stride not aligned as required";
+        case KQ_ERR_HIP: return "KQ_ERR_HIP: the HIP runtime rejected the launch";
+        default: return "unknown kq_status";
+    }
+}
+
+int kq_version(void) { return 100; }
+
+// Common front end of the bf16-activation entry points.
+static kq_status check_bf16_act(const void *x, int64_t tokens, int64_t d, int64_t ld_x) {
+    kq_status st = check_shape(tokens, d, ld_x);
+    if (st != KQ_OK) return st;
+    if (tokens == 0) return KQ_OK;
+    if (!x) return KQ_ERR_NULL;
+    if (!aligned(x, 16) || (ld_x * 2) % 16 != 0) return KQ_ERR_ALIGN;
+    return KQ_OK;
+}
+
+static kq_status check_mxfp4_out(const uint8_t *codes, const uint8_t *scales) {
+    if (!codes || !scales) return KQ_ERR_NULL;
+    if (!aligned(codes, 16)) return KQ_ERR_ALIGN;
+    return KQ_OK;
+}
+
+kq_status kq_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                             const float *lu, uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_bf16_act(x, tokens, d, ld_x);
+    if (st != KQ_OK || tokens == 0) return st;
+    if (!lu) return KQ_ERR_NULL;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    if (!aligned(lu, 4)) return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    return run(Bf16Src{(const uint16_t *)x, ld_x}, KronStage{lu, {}, {}, {}},
+               Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+}
+
+kq_status kq_transform_f32(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                           const float *lu, float *y, void *stream) {
+    kq_status st = check_bf16_act(x, tokens, d, ld_x);
+    if (st != KQ_OK || tokens == 0) return st;
+    if (!lu || !y) return KQ_ERR_NULL;
+    if (!aligned(lu, 4) || !aligned(y, 16)) return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    return run(Bf16Src{(const uint16_t *)x, ld_x}, KronStage{lu, {}, {}, {}}, F32Sink{y, d},
+               tokens, nb, stream);
+}
+
+kq_status kq_smooth_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          const float *mult, uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_bf16_act(x, tokens, d, ld_x);
+    if (st != KQ_OK || tokens == 0) return st;
+    if (!mult) return KQ_ERR_NULL;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    if (!aligned(mult, 16)) return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    return run(Bf16Src{(const uint16_t *)x, ld_x}, SmoothStage{mult, {}},
+               Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+}
+
+kq_status kq_fwht32_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_bf16_act(x, tokens, d, ld_x);
+    if (st != KQ_OK || tokens == 0) return st;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    const int nb = (int)(d / 32);
+    return run(Bf16Src{(const uint16_t *)x, ld_x}, FwhtStage{}, Mxfp4Sink{codes, scales, nb},
+               tokens, nb, stream);
+}
+
+kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t ld_y,
+                             uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_shape(tokens, d, ld_y);
+    if (st != KQ_OK || tokens == 0) return st;
+    if (!y) return KQ_ERR_NULL;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    if (!aligned(y, 16) || (ld_y * 4) % 16 != 0) return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    return run(F32Src{y, ld_y}, IdentityStage{}, Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+}
+
+kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_bf16_act(x, tokens, d, ld_x);
+    if (st != KQ_OK || tokens == 0) return st;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    const int nb = (int)(d / 32);
+    Plan pl;
+    if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
+    return launch(copy_ceiling_kernel<kUnitsInFlight>, pl, stream,
+                  Bf16Src{(const uint16_t *)x, ld_x}, codes, scales, (int)tokens, nb, pl.tstep);
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+"""Thin ctypes binding of ``libkq.so`` (the C ABI declared in ``include/kq.h``).
+
+Two layers, both argument marshalling only:
+
+* ``kq_*`` functions with the C names and signatures: raw device pointers
+  (ints), sizes and a stream handle; they return the ``kq_status`` code.
+* tensor helpers (``transform_quant`` ...): take torch tensors resident on the
+  GPU, allocate the outputs with torch, pass ``data_ptr()`` and torch's current
+  HIP stream, and raise :class:`KQError` on a non-OK status.
+
+Every step of the computation runs in the gfx950 kernels of ``libkq.so``.
+If the library is missing this module raises; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kq.h")
+
+KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP = 0, 1, 2, 3, 4
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_ST = ctypes.c_int
+
+# name -> (restype, argtypes), in the order of include/kq.h
+SIGNATURES = {
+    "kq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "kq_version": (ctypes.c_int, []),
+    "kq_transform_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kq_transform_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_smooth_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kq_fwht32_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_mxfp4_quant_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+}
+
+
+class KQError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"{name}: {status_str(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkq.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/kq.h declares."""
+    with open(HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)
+
+
+def status_str(status: int) -> str:
+    return lib().kq_status_str(status).decode()
+
+
+def version() -> int:
+    return lib().kq_version()
+
+
+# ---- C-named wrappers (pointers as ints) -----------------------------------
+def kq_transform_quant(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> int:
+    return lib().kq_transform_quant(x, tokens, d, ld_x, lu, codes, scales, stream)
+
+
+def kq_transform_f32(x, tokens, d, ld_x, lu, y, stream=None) -> int:
+    return lib().kq_transform_f32(x, tokens, d, ld_x, lu, y, stream)
+
+
+def kq_smooth_quant(x, tokens, d, ld_x, mult, codes, scales, stream=None) -> int:
+    return lib().kq_smooth_quant(x, tokens, d, ld_x, mult, codes, scales, stream)
+
+
+def kq_fwht32_quant(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
+    return lib().kq_fwht32_quant(x, tokens, d, ld_x, codes, scales, stream)
+
+
+def kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream=None) -> int:
+    return lib().kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream)
+
+
+def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
+    return lib().kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream)
+
+
+# ---- tensor helpers --------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(name: str, st: int) -> None:
+    if st != KQ_OK:
+        raise KQError(name, st)
+
+
+def _act(x, dtype_name: str):
+    torch = _torch()
+    want = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype_name]
+    if x.dtype != want or x.dim() != 2 or not x.is_cuda:
+        raise ValueError(f"expected a 2-D {want} GPU tensor, got {x.dtype} {tuple(x.shape)}")
+    if x.stride(1) != 1:
+        raise ValueError("the channel dimension must be contiguous")
+    return x.shape[0], x.stride(0)
+
+
+def _mxfp4_out(x, tokens: int, d: int, codes=None, scales=None):
+    torch = _torch()
+    if codes is None:
+        codes = torch.empty((tokens, d // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((tokens, d // 32), dtype=torch.uint8, device=x.device)
+    return codes, scales
+
+
+def transform_quant(x, lu, d: int | None = None, codes=None, scales=None):
+    """KroQuant block transform + MXFP4 of bf16 ``x`` [tokens][>=d]."""
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_transform_quant", kq_transform_quant(
+        x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+        _stream(x)))
+    return codes, scales
+
+
+def transform_f32(x, lu, d: int | None = None, y=None):
+    torch = _torch()
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    if y is None:
+        y = torch.empty((tokens, d), dtype=torch.float32, device=x.device)
+    _check("kq_transform_f32", kq_transform_f32(
+        x.data_ptr(), tokens, d, ld, lu.data_ptr(), y.data_ptr(), _stream(x)))
+    return y
+
+
+def smooth_quant(x, mult, d: int | None = None, codes=None, scales=None):
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_smooth_quant", kq_smooth_quant(
+        x.data_ptr(), tokens, d, ld, mult.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+        _stream(x)))
+    return codes, scales
+
+
+def fwht32_quant(x, d: int | None = None, codes=None, scales=None):
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_fwht32_quant", kq_fwht32_quant(
+        x.data_ptr(), tokens, d, ld, codes.data_ptr(), scales.data_ptr(), _stream(x)))
+    return codes, scales
+
+
+def mxfp4_quant_f32(y, d: int | None = None, codes=None, scales=None):
+    tokens, ld = _act(y, "f32")
+    d = y.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(y, tokens, d, codes, scales)
+    _check("kq_mxfp4_quant_f32", kq_mxfp4_quant_f32(
+        y.data_ptr(), tokens, d, ld, codes.data_ptr(), scales.data_ptr(), _stream(y)))
+    return codes, scales
+
+
+def copy_ceiling(x, d: int | None = None, codes=None, scales=None):
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_copy_ceiling", kq_copy_ceiling(
+        x.data_ptr(), tokens, d, ld, codes.data_ptr(), scales.data_ptr(), _stream(x)))
+    return codes, scales

@@ -1,0 +1,91 @@
+"""The C ABI: libkq.so loads, exports every function include/kq.h declares, and
+rejects bad arguments on the host before any HIP call.
+
+Nothing here touches a GPU: every call below fails validation (or is empty)
+and returns before the library makes its first HIP runtime call; the pointers
+passed are never dereferenced.
+"""
+import ctypes
+
+import pytest
+
+from mxfp4_activation_quantizer_amd import kq
+
+A16 = 0x10000   # a 16-byte-aligned dummy address, never dereferenced
+ODD = 0x10001   # misaligned dummy address
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = kq.lib()
+    declared = kq.declared_functions()
+    assert "kq_transform_quant" in declared and "kq_status_str" in declared
+    for name in declared:
+        assert hasattr(L, name), name
+    # the binding knows every declared function (and nothing undeclared)
+    assert set(kq.SIGNATURES) == set(declared)
+    # and the shared object's dynamic symbols include them
+    for name in declared:
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert kq.status_str(kq.KQ_OK) == "KQ_OK"
+    for st in (kq.KQ_ERR_NULL, kq.KQ_ERR_SHAPE, kq.KQ_ERR_ALIGN, kq.KQ_ERR_HIP):
+        assert kq.status_str(st).startswith("KQ_ERR_")
+    assert "unknown" in kq.status_str(99)
+    assert kq.version() >= 100
+
+
+QUANT_CALLS = {
+    "kq_transform_quant": lambda x, t, d, ld, c, s: kq.kq_transform_quant(x, t, d, ld, A16, c, s),
+    "kq_smooth_quant": lambda x, t, d, ld, c, s: kq.kq_smooth_quant(x, t, d, ld, A16, c, s),
+    "kq_fwht32_quant": lambda x, t, d, ld, c, s: kq.kq_fwht32_quant(x, t, d, ld, c, s),
+    "kq_copy_ceiling": lambda x, t, d, ld, c, s: kq.kq_copy_ceiling(x, t, d, ld, c, s),
+}
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_CALLS))
+def test_shape_errors(name):
+    f = QUANT_CALLS[name]
+    assert f(A16, -1, 64, 64, A16, A16) == kq.KQ_ERR_SHAPE
+    assert f(A16, 1 << 30, 64, 64, A16, A16) == kq.KQ_ERR_SHAPE
+    assert f(A16, 4, 0, 64, A16, A16) == kq.KQ_ERR_SHAPE
+    assert f(A16, 4, 48, 64, A16, A16) == kq.KQ_ERR_SHAPE      # d % 32 != 0
+    assert f(A16, 4, 64, 32, A16, A16) == kq.KQ_ERR_SHAPE      # ld < d
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_CALLS))
+def test_empty_is_ok_without_pointers(name):
+    assert QUANT_CALLS[name](None, 0, 64, 64, None, None) == kq.KQ_OK
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_CALLS))
+def test_null_and_alignment_errors(name):
+    f = QUANT_CALLS[name]
+    assert f(None, 4, 64, 64, A16, A16) == kq.KQ_ERR_NULL
+    assert f(A16, 4, 64, 64, None, A16) == kq.KQ_ERR_NULL
+    assert f(A16, 4, 64, 64, A16, None) == kq.KQ_ERR_NULL
+    assert f(ODD, 4, 64, 64, A16, A16) == kq.KQ_ERR_ALIGN
+    assert f(A16, 4, 64, 68, A16, A16) == kq.KQ_ERR_ALIGN      # row stride 136 B
+    assert f(A16, 4, 64, 64, ODD, A16) == kq.KQ_ERR_ALIGN
+
+
+def test_parameter_pointer_checks():
+    assert kq.kq_transform_quant(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
+    assert kq.kq_transform_quant(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
+    assert kq.kq_smooth_quant(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
+    assert kq.kq_smooth_quant(A16, 4, 64, 64, A16 + 4, A16, A16) == kq.KQ_ERR_ALIGN
+    assert kq.kq_transform_f32(A16, 4, 64, 64, A16, None) == kq.KQ_ERR_NULL
+    assert kq.kq_transform_f32(A16, 4, 64, 64, A16, A16 + 8) == kq.KQ_ERR_ALIGN
+    assert kq.kq_transform_f32(None, 0, 64, 64, None, None) == kq.KQ_OK
+    assert kq.kq_mxfp4_quant_f32(A16, 4, 64, 66, A16, A16) == kq.KQ_ERR_ALIGN
+    assert kq.kq_mxfp4_quant_f32(A16, 4, 64, 60, A16, A16) == kq.KQ_ERR_SHAPE
+    assert kq.kq_mxfp4_quant_f32(None, 4, 64, 64, A16, A16) == kq.KQ_ERR_NULL
+    assert kq.kq_mxfp4_quant_f32(None, 0, 64, 64, None, None) == kq.KQ_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kq.transform_quant(x, torch.zeros(30))

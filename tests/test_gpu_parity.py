@@ -1,0 +1,329 @@
+"""GPU parity: the gfx950 kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bars:
+  * bit-exact codes, scale bytes and fp32 values against the oracle's fixed
+    fp32 order (the order documented in include/kq.h);
+  * against the fp64 definition: transformed values within 1e-5 of
+    sum_i |x_i T_ik|, and at most 1e-4 of codes different, each by one
+    adjacent grid step at a rounding tie (tests/parity.py).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp4_activation_quantizer_amd import inputs, kq
+from parity import (assert_codes_within_tie_tolerance, to_gpu, to_gpu_bf16, unpack_codes,
+                    REL_Y)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _gpu_tq(x_bits, lu, d=None):
+    codes, scales = kq.transform_quant(to_gpu_bf16(x_bits), to_gpu(lu), d=d)
+    return _np(codes), _np(scales)
+
+
+# --------------------------------------------------------------------------
+# tiny workload (64 x 256)
+# --------------------------------------------------------------------------
+def test_tiny_bit_exact_vs_staged_order(torch_cuda):
+    x, lu = inputs.activation("tiny"), inputs.lu_params("tiny")
+    c, s = _gpu_tq(x, lu)
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(c, wc)
+
+
+def test_tiny_transform_values(torch_cuda):
+    x, lu = inputs.activation("tiny"), inputs.lu_params("tiny")
+    y = _np(kq.transform_f32(to_gpu_bf16(x), to_gpu(lu)))
+    np.testing.assert_array_equal(y.view(np.uint32),
+                                  oracle.transform(x, lu, oracle.STAGED32).view(np.uint32))
+    y64 = oracle.transform(x, lu, oracle.DENSE64)
+    bound = oracle.transform_absbound(x, lu)
+    assert np.all(np.abs(y.astype(np.float64) - y64) <= REL_Y * bound + 1e-30)
+
+
+def test_tiny_codes_vs_definition(torch_cuda):
+    x, lu = inputs.activation("tiny"), inputs.lu_params("tiny")
+    c, s = _gpu_tq(x, lu)
+    wc, ws = oracle.transform_quant(x, lu, oracle.DENSE64)
+    assert_codes_within_tie_tolerance(c, s, wc, ws, oracle.transform(x, lu, oracle.DENSE64),
+                                      oracle.transform_absbound(x, lu))
+
+
+# --------------------------------------------------------------------------
+# the quantizer stage over every bf16 value and around every rounding tie
+# --------------------------------------------------------------------------
+IDENTITY = np.array([0.0, 1.0, 0.0], np.float32)
+
+
+@pytest.mark.parametrize("arrangement", ["consecutive", "strided", "permuted"])
+def test_identity_params_every_bf16_value(torch_cuda, arrangement):
+    """With (l,u,v) = (0,1,0) every factor is I, so the kernel is plain MXFP4
+    of the bf16 input, up to the sign of zero (fma(0, q, -0) is +0 when q > 0,
+    in the oracle's staged order as on the GPU); all 65,536 bf16 patterns go
+    through it."""
+    pats = np.arange(65536, dtype=np.uint16)
+    if arrangement == "strided":
+        pats = pats.reshape(32, 2048).T.reshape(-1)
+    elif arrangement == "permuted":
+        pats = np.random.default_rng(0).permutation(pats)
+    x = pats.reshape(256, 256)
+    lu = np.tile(IDENTITY, (8, 5, 1))
+    c, s = _gpu_tq(x, lu)
+    sc, ss = oracle.transform_quant(x, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s, ss)
+    np.testing.assert_array_equal(c, sc)
+    wc, ws = oracle.mxfp4_quant(inputs.bf16_bits_to_f32(x))
+    np.testing.assert_array_equal(s, ws)
+    u, wu = unpack_codes(c), unpack_codes(wc)
+    differ = u != wu
+    assert np.all((u[differ] & 7) == 0) and np.all((wu[differ] & 7) == 0)
+    assert differ.sum() <= 4
+    assert (s == 0xFF).any() and (s == 0).any()
+
+
+def _neighbours(v, k):
+    out = [v]
+    up = down = np.float32(v)
+    for _ in range(k):
+        up = np.nextafter(up, np.float32(np.inf))
+        down = np.nextafter(down, np.float32(-np.inf))
+        out += [up, down]
+    return out
+
+
+def test_quantizer_at_rounding_ties_all_scales(torch_cuda):
+    """fp32 values at and next to every E2M1 midpoint and grid value, at
+    every scale exponent, in blocks whose amax pins the scale."""
+    qs = []
+    for m in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1, 1.5, 2, 3, 4, 6]:
+        qs += _neighbours(np.float32(m), 3)
+    qs = np.array(qs, np.float32)
+    qs = np.concatenate([qs, -qs])
+    rows = []
+    for e in range(-127, 126):
+        pilot = np.float32(np.ldexp(4.0, e)) if e > -127 else np.float32(np.ldexp(4.0, -127))
+        vals = (qs.astype(np.float64) * 2.0 ** e).astype(np.float32)
+        for i in range(0, len(vals), 31):
+            blk = np.zeros(32, np.float32)
+            chunk = vals[i:i + 31]
+            blk[:len(chunk)] = chunk
+            blk[31] = pilot
+            rows.append(blk)
+    while len(rows) % 8:
+        rows.append(np.zeros(32, np.float32))
+    y = np.stack(rows).reshape(-1, 256)
+    c, s = kq.mxfp4_quant_f32(to_gpu(y))
+    wc, ws = oracle.mxfp4_quant(y)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+
+
+def test_quantizer_random_fp32(torch_cuda):
+    g = np.random.default_rng(1)
+    n = 512 * 1024
+    y = (g.standard_normal(n) * 2.0 ** g.integers(-140, 120, n)).astype(np.float32)
+    # sprinkle zeros, negative zeros, subnormals, huge values and specials
+    idx = g.choice(n, 4000, replace=False)
+    y[idx[:500]] = 0.0
+    y[idx[500:1000]] = -0.0
+    y[idx[1000:1500]] = (g.standard_normal(500) * 2.0 ** -140).astype(np.float32)
+    y[idx[1500:1600]] = np.float32(3.3e38)
+    y[idx[1600:1650]] = np.nan
+    y[idx[1650:1700]] = np.inf
+    y[idx[1700:1750]] = -np.inf
+    y = y.reshape(-1, 512)
+    c, s = kq.mxfp4_quant_f32(to_gpu(y))
+    wc, ws = oracle.mxfp4_quant(y)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+
+
+# --------------------------------------------------------------------------
+# transform wiring
+# --------------------------------------------------------------------------
+def test_power_of_two_diagonal_params_are_exact(torch_cuda):
+    """(0, 2^m, 0) factors give an exact diagonal power-of-two T: the kernel
+    must equal the fp64 definition bit for bit."""
+    g = np.random.default_rng(2)
+    nb = 12
+    lu = np.zeros((nb, 5, 3), np.float32)
+    lu[:, :, 1] = 2.0 ** g.integers(-3, 4, (nb, 5))
+    x = inputs.f64_to_bf16_bits(g.standard_normal((100, nb * 32)) * 5)
+    c, s = _gpu_tq(x, lu)
+    wc, ws = oracle.transform_quant(x, lu, oracle.DENSE64)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(c, wc)
+
+
+def test_spike_through_hadamard_start(torch_cuda):
+    """LRQ-DiT Lemma 1 with a Hadamard: a spike of 30 becomes 30/sqrt(32) =
+    5.3 everywhere, so scale byte 127 and every code magnitude is 6."""
+    nb = 4
+    lu = inputs.hadamard_init(nb)
+    x = np.zeros((32, nb * 32), np.float64)
+    for t in range(32):
+        x[t, (t % nb) * 32 + t] = 30.0 if t % 2 else -30.0
+    xb = inputs.f64_to_bf16_bits(x)
+    c, s = _gpu_tq(xb, lu)
+    for t in range(32):
+        j = t % nb
+        assert s[t, j] == 127
+        assert np.all(unpack_codes(c)[t, j * 32:(j + 1) * 32] & 7 == 7)
+        others = [k for k in range(nb) if k != j]
+        assert np.all(s[t, others] == 0)
+
+
+def test_shear_on_each_bit(torch_cuda):
+    """A lone lower shear on bit b mixes channel pairs (k, k ^ 2^b) only."""
+    g = np.random.default_rng(3)
+    x = inputs.f64_to_bf16_bits(g.standard_normal((8, 32)))
+    for b in range(5):
+        lu = np.tile(IDENTITY, (1, 5, 1))
+        lu[0, b, 0] = 0.75
+        y = _np(kq.transform_f32(to_gpu_bf16(x), to_gpu(lu)))
+        np.testing.assert_array_equal(y, oracle.transform(x, lu, oracle.STAGED32))
+
+
+# --------------------------------------------------------------------------
+# shapes, strides, edge cases
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("tokens,nb,pad", [(1, 1, 0), (3, 2, 8), (77, 3, 0), (300, 5, 24),
+                                           (129, 36, 0), (65, 96, 8), (33, 97, 0), (5, 384, 16),
+                                           (1000, 7, 0)])
+def test_ragged_shapes_and_strides(torch_cuda, tokens, nb, pad):
+    torch = torch_cuda
+    g = np.random.default_rng(tokens * 1000 + nb)
+    d = nb * 32
+    xf = g.standard_normal((tokens, d + pad)) * np.exp(g.standard_normal((tokens, 1)))
+    x = inputs.f64_to_bf16_bits(xf)
+    x[:, d:] = 0x7FC0                       # NaN padding must never be read
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    # outputs inside canary-filled buffers
+    cbuf = torch.full((tokens * d // 2 + 64,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    sbuf = torch.full((tokens * nb + 64,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    codes = cbuf[32:32 + tokens * d // 2].view(tokens, d // 2)
+    scales = sbuf[32:32 + tokens * nb].view(tokens, nb)
+    kq.transform_quant(to_gpu_bf16(x), to_gpu(lu), d=d, codes=codes, scales=scales)
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32, d=d)
+    np.testing.assert_array_equal(_np(scales), ws)
+    np.testing.assert_array_equal(_np(codes), wc)
+    cb, sb = _np(cbuf), _np(sbuf)
+    assert np.all(cb[:32] == 0xA5) and np.all(cb[32 + tokens * d // 2:] == 0xA5)
+    assert np.all(sb[:32] == 0x5A) and np.all(sb[32 + tokens * nb:] == 0x5A)
+
+
+def test_empty_input(torch_cuda):
+    torch = torch_cuda
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda:0")
+    lu = to_gpu(inputs.hadamard_init(2))
+    c, s = kq.transform_quant(x, lu)
+    assert c.shape == (0, 32) and s.shape == (0, 2)
+
+
+def test_nonfinite_and_overflow_blocks(torch_cuda):
+    nb = 4
+    x = np.full((6, nb * 32), 0x3F80, np.uint16)  # 1.0
+    x[0, 5] = 0x7FC0          # NaN in block 0
+    x[1, 40] = 0x7F80         # +Inf in block 1
+    x[2, 70] = 0xFF80         # -Inf in block 2
+    x[3, 96:128] = 0x7F7F     # bf16 max everywhere in block 3: the transform overflows
+    x[4, :] = 0x0000
+    x[5, :] = 0x8000          # -0.0
+    lu = inputs.hadamard_init(nb)
+    c, s = _gpu_tq(x, lu)
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(c, wc)
+    assert s[0, 0] == s[1, 1] == s[2, 2] == 0xFF
+    assert s[4, 0] == 0 and s[5, 0] == 0
+
+
+def test_deterministic(torch_cuda):
+    x, lu = inputs.activation("tiny"), inputs.lu_params("tiny")
+    a = _gpu_tq(x, lu)
+    b = _gpu_tq(x, lu)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------
+# baselines and the ceiling kernel
+# --------------------------------------------------------------------------
+def test_smooth_quant_bit_exact(torch_cuda):
+    x = inputs.activation("tiny")
+    m = inputs.smooth_multipliers(x)
+    c, s = kq.smooth_quant(to_gpu_bf16(x), to_gpu(m))
+    wc, ws = oracle.smooth_quant(x, m)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+
+
+def test_fwht32_quant_bit_exact_and_vs_definition(torch_cuda):
+    x = inputs.activation("tiny")
+    c, s = kq.fwht32_quant(to_gpu_bf16(x))
+    c, s = _np(c), _np(s)
+    wc, ws = oracle.fwht32_quant(x, oracle.STAGED32)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(c, wc)
+    dc, ds = oracle.fwht32_quant(x, oracle.DENSE64)
+    xf = np.abs(inputs.bf16_bits_to_f32(x).astype(np.float64))
+    bound = np.repeat(xf.reshape(x.shape[0], -1, 32).sum(2), 32, axis=1) / np.sqrt(32)
+    assert_codes_within_tie_tolerance(c, s, dc, ds, oracle.fwht32(x, oracle.DENSE64), bound)
+
+
+def test_copy_ceiling_touches_every_unit(torch_cuda):
+    x = inputs.activation("tiny")
+    c, s = kq.copy_ceiling(to_gpu_bf16(x))
+    w = x.view(np.uint32).reshape(64, 8, 4, 4)
+    f = w[:, :, 0] ^ w[:, :, 1] ^ w[:, :, 2] ^ w[:, :, 3]
+    np.testing.assert_array_equal(_np(c).view(np.uint32).reshape(64, 8, 4), f)
+    fs = (f[..., 0] ^ f[..., 1] ^ f[..., 2] ^ f[..., 3]) & 0xFF
+    np.testing.assert_array_equal(_np(s), fs.astype(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["pixart", "flux_attn", "flux_mlp"])
+def test_full_size_workload_sampled(torch_cuda, name):
+    _log(f"full-size {name}: generating")
+    x = inputs.activation(name)
+    lu = inputs.lu_params(name)
+    c, s = _gpu_tq(x, lu)
+    rows = np.sort(np.random.default_rng(7).choice(x.shape[0], 96, replace=False))
+    rows[:2] = [0, 1]
+    rows[-1] = x.shape[0] - 1
+    xs = x[rows]
+    _log(f"full-size {name}: oracle on {len(rows)} rows")
+    wc, ws = oracle.transform_quant(xs, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s[rows], ws)
+    np.testing.assert_array_equal(c[rows], wc)
+    dc, ds = oracle.transform_quant(xs, lu, oracle.DENSE64)
+    n_s, n_c = assert_codes_within_tie_tolerance(
+        c[rows], s[rows], dc, ds, oracle.transform(xs, lu, oracle.DENSE64),
+        oracle.transform_absbound(xs, lu))
+    _log(f"full-size {name}: vs fp64 definition {n_s} scale / {n_c} code tie differences")
+    # whole-tensor properties at full size: every finite block's largest code
+    # magnitude is 4 or 6, and no scale is NaN for finite input
+    assert not (s == 0xFF).any()
+    mags = (unpack_codes(c) & 7).reshape(x.shape[0], -1, 32).max(axis=2)
+    assert np.all((mags >= 6) | (s == 0))
