@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the fused KroQuant transform + MXFP4 quantizer on one MI355X.
+
+One step = one kq_transform_quant call over one 4608 x 3072 bf16 activation
+(the FLUX attention-projection input shape): every 32-channel block is
+multiplied by its Kronecker-structured 32x32 transform and quantized to MXFP4.
+
+Inputs are seeded synthetic data (mxfp4_activation_quantizer_amd.inputs),
+copied to the GPU before timing.  Steps rotate over several buffer sets whose
+total exceeds twice the 256 MB Infinity Cache, so every step reads its input
+from HBM, not from a cache that the previous step warmed.
+
+Prints one JSON line.  `value` is GB/s of algorithmic traffic (2 B read +
+0.5 B + 1/32 B written per element) over the timed region: W untimed warmup
+steps, then exactly K steps bracketed by synchronisations, timed with HIP
+events on the stream the kernels run on.  The line also carries the roofline
+of the kernel, the CPU oracle timed on the host, and the same-traffic peers
+(per-channel scaling, FWHT32, a copy ceiling) on the same input.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20         # Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="flux_attn",
+                    choices=["pixart", "flux_attn", "flux_mlp"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-peers", action="store_true", help="skip the peer kernels")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="run only the timed steps of one kernel (for profilers)")
+    ap.add_argument("--kernel", default="kq_transform_quant",
+                    choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
+                             "kq_fwht32_quant", "kq_copy_ceiling"],
+                    help="the entry point --kernel-only times")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 64 MiB device-to-device copy, the known-size "
+                         "reference for the HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(token rows shard with no exchange; see the design notes). "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if world != 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mxfp4_activation_quantizer_amd import inputs, kq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 64 << 20
+        srcs = [torch.ones(n // 2, dtype=torch.bfloat16, device=dev) for _ in range(8)]
+        dsts = [torch.empty_like(srcs[0]) for _ in range(8)]
+        for i in range(args.steps):
+            dsts[i % 8].copy_(srcs[i % 8])
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return 0
+    w = inputs.WORKLOADS[args.workload]
+    T, d, nb = w.tokens, w.d, w.blocks
+    nbytes = w.algorithmic_bytes
+
+    x_bits = inputs.activation(args.workload)
+    lu = inputs.lu_params(args.workload)
+    mult = inputs.smooth_multipliers(x_bits)
+
+    set_bytes = nbytes
+    R = max(2, -(-2 * MALL_BYTES // set_bytes))
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    codes = [torch.empty((T, d // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    scales = [torch.empty((T, nb), dtype=torch.uint8, device=dev) for _ in range(R)]
+    lu_d = torch.from_numpy(lu).to(dev)
+    mult_d = torch.from_numpy(mult).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    L = kq.lib()
+
+    def argsets(fn_name):
+        out = []
+        for i in range(R):
+            xp, cp, scp = xs[i].data_ptr(), codes[i].data_ptr(), scales[i].data_ptr()
+            if fn_name in ("kq_transform_quant", "kq_transform_quant_mfma"):
+                out.append((xp, T, d, d, lu_d.data_ptr(), cp, scp, sp))
+            elif fn_name == "kq_smooth_quant":
+                out.append((xp, T, d, d, mult_d.data_ptr(), cp, scp, sp))
+            else:
+                out.append((xp, T, d, d, cp, scp, sp))
+        return out
+
+    def timed(fn_name, steps, warmup):
+        fn = getattr(L, fn_name)
+        a = argsets(fn_name)
+        for i in range(warmup):
+            st = fn(*a[i % R])
+            if st != 0:
+                raise kq.KQError(fn_name, st)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(*a[i % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per launch
+
+    if args.kernel_only:
+        ms = timed(args.kernel, args.steps, args.warmup)
+        print(json.dumps({"kernel": args.kernel, "ms_per_step": ms,
+                          "GBps": nbytes / (ms * 1e-3) / 1e9}), flush=True)
+        return 0
+    ms = timed("kq_transform_quant", args.steps, args.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    extra = {}
+    if not args.no_peers:
+        for name, fn_name in [("transform_quant_mfma", "kq_transform_quant_mfma"),
+                              ("smooth_quant", "kq_smooth_quant"),
+                              ("fwht32_quant", "kq_fwht32_quant"),
+                              ("copy_ceiling", "kq_copy_ceiling")]:
+            pms = timed(fn_name, args.steps, args.warmup)
+            extra[name] = {"ms_per_step": round(pms, 6),
+                           "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
+        extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+
+    src_hash = kernel_source_hash()
+    traffic = load_traffic("kq_transform_quant", args.workload, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": nbytes}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle  # CPU baseline leg only
+        cores = len(os.sched_getaffinity(0))
+        oracle.transform_quant(x_bits[:64], lu, oracle.STAGED32, threads=cores)  # warm
+        times = []
+        deadline = time.perf_counter() + 10.0
+        while len(times) < 3 or (time.perf_counter() < deadline and len(times) < 20):
+            t0 = time.perf_counter()
+            oracle.transform_quant(x_bits, lu, oracle.STAGED32, threads=cores)
+            times.append(time.perf_counter() - t0)
+        tmed = sorted(times)[len(times) // 2]
+        cpu = {"value": round(nbytes / tmed / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"the whole {T}x{d} workload, oracle fixed-fp32-order mode, "
+                         f"median of {len(times)} runs on {cores} threads"}
+
+    line = {
+        "metric": "fused Kron-transform+MXFP4 quantize GB/s & % HBM peak, 4608x3072 bf16, 1 GPU",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_{T}x{d}", "tokens": T, "channels": d,
+                   "blocks_per_row": nb, "input": "bf16", "output": "mxfp4 (e2m1 + e8m0/32)",
+                   "rotating_buffer_sets": R, "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "peers": extra,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -93,6 +93,21 @@ kq_status kq_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t l
                              void *stream);
 
 /*
+ * kq_transform_quant_mfma — the same quantizer with the block transform run
+ * as a dense 32x32 product on the matrix cores, the formulation of the
+ * KroQuant summary ("Approach": a single tensor-core GEMM per block) and
+ * abstract ("small tensor-core GEMMs").  Same arguments, layouts and errors
+ * as kq_transform_quant.  T_j is materialised in fp32 and split into three
+ * bf16 terms; the products accumulate in fp32 in the matrix core's own order,
+ * so values agree with the exact y = x * T_j to within fp32 rounding (not
+ * bit-for-bit with kq_transform_quant), and codes may differ from it only at
+ * E2M1 rounding ties.
+ */
+kq_status kq_transform_quant_mfma(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                                  const float *lu, uint8_t *codes, uint8_t *scales,
+                                  void *stream);
+
+/*
  * kq_transform_f32 — the same device transform as kq_transform_quant with an
  * fp32 store instead of the quantizer: y fp32 [tokens][d], 16-byte aligned.
  * For checking the transform stage on its own.

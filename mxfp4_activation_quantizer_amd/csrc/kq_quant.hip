@@ -13,8 +13,8 @@
 // ... which all belong to block j = g mod nb: the per-block constants (five
 // shears and the 32-entry diagonal) are derived once per lane and stay in
 // VGPRs, and consecutive units of a lane are tstep = L / nb tokens apart.
-// Each lane issues the loads of P units before computing any of them, so
-// several 64-byte requests per lane are in flight at once.
+// Each lane issues the loads of all its units before computing any of them,
+// so several 64-byte requests per lane overlap the arithmetic.
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -27,7 +27,6 @@
 namespace kq {
 
 constexpr int kBlockThreads = 256;  // 4 waves of 64 lanes
-constexpr int kUnitsInFlight = 2;   // P: units whose loads are issued together
 
 // ---------------------------------------------------------------------------
 // Sources: where a unit's 32 input values come from.
@@ -39,7 +38,7 @@ struct Bf16Src {
     __device__ __forceinline__ void load(int t, int j, Raw &r) const {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(x + (int64_t)t * ld + (int64_t)j * 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(p + i);
+        for (int i = 0; i < 4; ++i) r.v[i] = p[i];
     }
     __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
 #pragma unroll
@@ -59,7 +58,7 @@ struct F32Src {
     __device__ __forceinline__ void load(int t, int j, Raw &r) const {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(y + (int64_t)t * ld + (int64_t)j * 32);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r.v[i] = __builtin_nontemporal_load(p + i);
+        for (int i = 0; i < 8; ++i) r.v[i] = p[i];
     }
     __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
 #pragma unroll
@@ -81,9 +80,14 @@ struct F32Src {
 // bit, then one multiply per element by d_k = prod_b (bit b of k ? 1/u_b : u_b).
 struct KronStage {
     const float *lu;  // [nb][5][3]
+    float p[15];      // raw (l, u, v) x 5 of this lane's block
     float l[5], w[5], dk[32];
-    __device__ __forceinline__ void setup(int j) {
-        const float *p = lu + (int64_t)j * 15;
+    __device__ __forceinline__ void fetch(int j) {
+        const float *src = lu + (int64_t)j * 15;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) p[i] = src[i];
+    }
+    __device__ __forceinline__ void setup() {
         float u[5], iu[5];
 #pragma unroll
         for (int b = 0; b < 5; ++b) {
@@ -127,7 +131,7 @@ struct KronStage {
 struct SmoothStage {
     const float *mult;  // [d]
     float m[32];
-    __device__ __forceinline__ void setup(int j) {
+    __device__ __forceinline__ void fetch(int j) {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(mult + (int64_t)j * 32);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -136,6 +140,7 @@ struct SmoothStage {
             for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
         }
     }
+    __device__ __forceinline__ void setup() {}
     __device__ __forceinline__ void apply(float (&z)[32]) const {
 #pragma unroll
         for (int k = 0; k < 32; ++k) z[k] = z[k] * m[k];
@@ -145,7 +150,8 @@ struct SmoothStage {
 // Orthonormal 32-point Walsh-Hadamard (Sylvester order, LRQ-DiT Eq. (3)):
 // five add/subtract stages, then one multiply by fl32(1/sqrt(32)).
 struct FwhtStage {
-    __device__ __forceinline__ void setup(int) {}
+    __device__ __forceinline__ void fetch(int) {}
+    __device__ __forceinline__ void setup() {}
     __device__ __forceinline__ void apply(float (&z)[32]) const {
 #pragma unroll
         for (int b = 0; b < 5; ++b) {
@@ -165,7 +171,8 @@ struct FwhtStage {
 };
 
 struct IdentityStage {
-    __device__ __forceinline__ void setup(int) {}
+    __device__ __forceinline__ void fetch(int) {}
+    __device__ __forceinline__ void setup() {}
     __device__ __forceinline__ void apply(float (&)[32]) const {}
 };
 
@@ -182,7 +189,7 @@ struct Mxfp4Sink {
         mxfp4_block(y, c, s);
         const int64_t unit = (int64_t)t * nb + j;
         __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(codes) + unit);
-        scales[unit] = (uint8_t)s;
+        __builtin_nontemporal_store((uint8_t)s, scales + unit);
     }
 };
 
@@ -196,59 +203,65 @@ struct F32Sink {
     }
 };
 
+// Same-traffic ceiling: no transform and no quantizer; the 16 code bytes are
+// the XOR of the unit's fp32 bit patterns eight at a time, the scale byte the
+// low byte of their XOR.  Same loads, same stores, almost no arithmetic.
+struct FoldSink {
+    uint8_t *codes;
+    uint8_t *scales;
+    int nb;
+    __device__ __forceinline__ void store(int t, int j, const float (&z)[32]) const {
+        uint32_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t f = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f ^= __float_as_uint(z[8 * q + k]);
+            c[q] = f;
+        }
+        const int64_t unit = (int64_t)t * nb + j;
+        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, reinterpret_cast<u32x4 *>(codes) + unit);
+        __builtin_nontemporal_store((uint8_t)(c[0] ^ c[1] ^ c[2] ^ c[3]), scales + unit);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // The kernel template.
+//
+// A lane owns up to NU units of block j, tstep tokens apart (units g, g + L,
+// ... of the flattened unit index, L the grid's lane count).  It issues the
+// loads of all its units first, then unpacks, transforms, quantizes and stores
+// them in order, each as soon as its own data has arrived: the code is
+// straight-line, so the compiler's memory wait before unit k counts exactly
+// the requests issued after it, and the arithmetic of unit k overlaps the
+// flight of units k+1.. and the loads of other waves.  Lanes past the end
+// repeat their last unit (same bytes to the same place), so no lane branches.
 // ---------------------------------------------------------------------------
-template <class Src, class Stage, class Sink, int P>
+template <class Src, class Stage, class Sink, int NU>
 __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, Stage stage, Sink sink,
                                                               int tokens, int nb, int tstep) {
     const int g = blockIdx.x * kBlockThreads + threadIdx.x;
     const int j = g % nb;
-    int t = g / nb;
-    if (t >= tokens) return;
-    stage.setup(j);
-    for (; t < tokens; t += P * tstep) {
-        typename Src::Raw raw[P];
+    const int t0 = g / nb;
+    if (t0 >= tokens) return;
+    const int avail = (tokens - 1 - t0) / tstep + 1;
+    const int cnt = avail < NU ? avail : NU;
+    const int last = t0 + (cnt - 1) * tstep;
+    // Parameter loads first, then every data load; the scheduling barrier
+    // keeps all of them ahead of the arithmetic (left alone, the scheduler
+    // sinks later units' loads below earlier units' math to save registers).
+    stage.fetch(j);
+    typename Src::Raw buf[NU];
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-            if (t + p * tstep < tokens) src.load(t + p * tstep, j, raw[p]);
+    for (int k = 0; k < NU; ++k) src.load(k < cnt ? t0 + k * tstep : last, j, buf[k]);
+    __builtin_amdgcn_sched_barrier(0);
+    stage.setup();
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int tt = t + p * tstep;
-            if (tt < tokens) {
-                float z[32];
-                Src::unpack(raw[p], z);
-                stage.apply(z);
-                sink.store(tt, j, z);
-            }
-        }
-    }
-}
-
-// Same-traffic ceiling: identical mapping and byte counts, output is an XOR
-// fold of the input instead of the quantizer.
-template <int P>
-__global__ __launch_bounds__(kBlockThreads) void copy_ceiling_kernel(Bf16Src src, uint8_t *codes,
-                                                                     uint8_t *scales, int tokens,
-                                                                     int nb, int tstep) {
-    const int g = blockIdx.x * kBlockThreads + threadIdx.x;
-    const int j = g % nb;
-    int t = g / nb;
-    for (; t < tokens; t += P * tstep) {
-        Bf16Src::Raw raw[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-            if (t + p * tstep < tokens) src.load(t + p * tstep, j, raw[p]);
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int tt = t + p * tstep;
-            if (tt < tokens) {
-                const u32x4 f = raw[p].v[0] ^ raw[p].v[1] ^ raw[p].v[2] ^ raw[p].v[3];
-                const int64_t unit = (int64_t)tt * nb + j;
-                __builtin_nontemporal_store(f, reinterpret_cast<u32x4 *>(codes) + unit);
-                scales[unit] = (uint8_t)(f[0] ^ f[1] ^ f[2] ^ f[3]);
-            }
-        }
+    for (int k = 0; k < NU; ++k) {
+        float z[32];
+        Src::unpack(buf[k], z);
+        stage.apply(z);
+        sink.store(k < cnt ? t0 + k * tstep : last, j, z);
     }
 }
 
@@ -265,20 +278,23 @@ static int gcd_int(int a, int b) {
 }
 
 struct Plan {
+    int nu;     // units per lane (a compiled instantiation: 1, 2, 4 or 8)
     int grid;   // workgroups
     int tstep;  // tokens between consecutive units of a lane
 };
 
-// Units per lane the grid is sized for.  KQ_UNITS_PER_LANE (read once)
-// overrides the default for launch-geometry sweeps.
+// Units per lane: 4 by default (enough requests in flight per lane to cover
+// the memory latency, while the per-lane constant setup is amortised over
+// four blocks).  KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for
+// launch-geometry sweeps.
 static int units_per_lane() {
     static int cached = 0;
     if (cached == 0) {
-        int v = 2;
+        int v = 4;
         const char *e = getenv("KQ_UNITS_PER_LANE");
         if (e) {
             int p = atoi(e);
-            if (p >= 1 && p <= 64) v = p;
+            if (p == 1 || p == 2 || p == 4 || p == 8) v = p;
         }
         cached = v;
     }
@@ -286,17 +302,18 @@ static int units_per_lane() {
 }
 
 static bool plan_launch(int64_t tokens, int nb, Plan &pl) {
-    // The lane count must be a multiple of nb: grid a multiple of m.
+    // The lane count must be a multiple of nb (so a lane keeps one block):
+    // the grid is a multiple of m = nb / gcd(nb, threads per workgroup).
     const int64_t m = nb / gcd_int(nb, kBlockThreads);
     const int64_t units = tokens * nb;
-    const int64_t per_wg = (int64_t)kBlockThreads * units_per_lane();
+    pl.nu = units_per_lane();
+    const int64_t per_wg = (int64_t)kBlockThreads * pl.nu;
     int64_t grid = (units + per_wg - 1) / per_wg;
     grid = (grid + m - 1) / m * m;
     if (grid < m) grid = m;
-    const int64_t lanes = grid * kBlockThreads;
     if (grid > INT32_MAX / kBlockThreads) return false;
     pl.grid = (int)grid;
-    pl.tstep = (int)(lanes / nb);
+    pl.tstep = (int)(grid * kBlockThreads / nb);
     return true;
 }
 
@@ -323,8 +340,13 @@ static kq_status run(const Src &src, const Stage &stage, const Sink &sink, int64
                      void *stream) {
     Plan pl;
     if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
-    return launch(block_kernel<Src, Stage, Sink, kUnitsInFlight>, pl, stream, src, stage, sink,
-                  (int)tokens, nb, pl.tstep);
+    const int t = (int)tokens;
+    switch (pl.nu) {
+        case 1: return launch(block_kernel<Src, Stage, Sink, 1>, pl, stream, src, stage, sink, t, nb, pl.tstep);
+        case 2: return launch(block_kernel<Src, Stage, Sink, 2>, pl, stream, src, stage, sink, t, nb, pl.tstep);
+        case 8: return launch(block_kernel<Src, Stage, Sink, 8>, pl, stream, src, stage, sink, t, nb, pl.tstep);
+        default: return launch(block_kernel<Src, Stage, Sink, 4>, pl, stream, src, stage, sink, t, nb, pl.tstep);
+    }
 }
 
 }  // namespace kq
@@ -424,10 +446,8 @@ kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x
     if (st != KQ_OK || tokens == 0) return st;
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     const int nb = (int)(d / 32);
-    Plan pl;
-    if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
-    return launch(copy_ceiling_kernel<kUnitsInFlight>, pl, stream,
-                  Bf16Src{(const uint16_t *)x, ld_x}, codes, scales, (int)tokens, nb, pl.tstep);
+    return run(Bf16Src{(const uint16_t *)x, ld_x}, IdentityStage{}, FoldSink{codes, scales, nb},
+               tokens, nb, stream);
 }
 
 }  // extern "C"

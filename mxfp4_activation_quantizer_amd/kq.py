@@ -32,6 +32,7 @@ SIGNATURES = {
     "kq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kq_version": (ctypes.c_int, []),
     "kq_transform_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kq_transform_quant_mfma": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_transform_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kq_smooth_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_fwht32_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
@@ -84,6 +85,10 @@ def version() -> int:
 # ---- C-named wrappers (pointers as ints) -----------------------------------
 def kq_transform_quant(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> int:
     return lib().kq_transform_quant(x, tokens, d, ld_x, lu, codes, scales, stream)
+
+
+def kq_transform_quant_mfma(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> int:
+    return lib().kq_transform_quant_mfma(x, tokens, d, ld_x, lu, codes, scales, stream)
 
 
 def kq_transform_f32(x, tokens, d, ld_x, lu, y, stream=None) -> int:
@@ -147,6 +152,17 @@ def transform_quant(x, lu, d: int | None = None, codes=None, scales=None):
     d = x.shape[1] if d is None else d
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
     _check("kq_transform_quant", kq_transform_quant(
+        x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+        _stream(x)))
+    return codes, scales
+
+
+def transform_quant_mfma(x, lu, d: int | None = None, codes=None, scales=None):
+    """The same quantizer with the block transform on the matrix cores."""
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_transform_quant_mfma", kq_transform_quant_mfma(
         x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
         _stream(x)))
     return codes, scales

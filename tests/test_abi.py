@@ -38,6 +38,8 @@ def test_status_strings():
 
 QUANT_CALLS = {
     "kq_transform_quant": lambda x, t, d, ld, c, s: kq.kq_transform_quant(x, t, d, ld, A16, c, s),
+    "kq_transform_quant_mfma": lambda x, t, d, ld, c, s: kq.kq_transform_quant_mfma(
+        x, t, d, ld, A16, c, s),
     "kq_smooth_quant": lambda x, t, d, ld, c, s: kq.kq_smooth_quant(x, t, d, ld, A16, c, s),
     "kq_fwht32_quant": lambda x, t, d, ld, c, s: kq.kq_fwht32_quant(x, t, d, ld, c, s),
     "kq_copy_ceiling": lambda x, t, d, ld, c, s: kq.kq_copy_ceiling(x, t, d, ld, c, s),
@@ -73,6 +75,8 @@ def test_null_and_alignment_errors(name):
 def test_parameter_pointer_checks():
     assert kq.kq_transform_quant(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
     assert kq.kq_transform_quant(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
+    assert kq.kq_transform_quant_mfma(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
+    assert kq.kq_transform_quant_mfma(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
     assert kq.kq_smooth_quant(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
     assert kq.kq_smooth_quant(A16, 4, 64, 64, A16 + 4, A16, A16) == kq.KQ_ERR_ALIGN
     assert kq.kq_transform_f32(A16, 4, 64, 64, A16, None) == kq.KQ_ERR_NULL
