@@ -26,15 +26,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 // Largest |y| over a 32-value block.  llvm.maximum propagates NaN (unlike
-// fmaxf), so a NaN anywhere in the block makes amax NaN; gfx950 issues this
-// chain as v_maximum3_f32 with |.| source modifiers, two values per op.
+// fmaxf), so a NaN anywhere in the block makes amax NaN.  Written as a chain
+// that folds two new values per step, which gfx950 issues as one
+// v_maximum3_f32 with |.| source modifiers per step.
 __device__ __forceinline__ float block_amax(const float (&y)[32]) {
     float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
 #pragma unroll
     for (int k = 2; k < 32; k += 2)
-        m = __builtin_elementwise_maximum(
-            m, __builtin_elementwise_maximum(__builtin_fabsf(y[k]), __builtin_fabsf(y[k + 1])));
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(y[k])),
+                                          __builtin_fabsf(y[k + 1]));
     return m;
+}
+
+// Correctly rounded fp32 reciprocal.  For |u| in [2^-126, 2^126) (biased
+// exponent 1..252) one fused correction of the hardware estimate,
+// r + r*(1 - u*r), equals IEEE 1/u bit for bit (checked exhaustively over all
+// fp32 inputs on gfx950); any other u takes the IEEE division.
+__device__ __forceinline__ float rcp_rn(float u) {
+    const uint32_t ex = (__float_as_uint(u) >> 23) & 0xffu;
+    if (__builtin_expect(ex - 1u < 252u, 1)) {
+        const float r = __builtin_amdgcn_rcpf(u);
+        return __builtin_fmaf(__builtin_fmaf(-u, r, 1.0f), r, r);
+    }
+    return 1.0f / u;
 }
 
 // E8M0 scale byte of the MXFP4 block: e = floor(log2 amax) - 2 clamped to

@@ -15,10 +15,16 @@
 // fixed order.  In the accumulator lane l holds token l%32's outputs
 // k = 8*(r/4) + 4*(l/32) + r%4, r = 0..15; lanes l and l^32 share a token.
 //
-// Workgroups: 4 waves on the same block, consecutive 32-token tiles.  The
-// workgroup index is mapped so that all blocks of a tile group run on the
-// same XCD (workgroups go to the 8 XCDs round-robin), so the 16-byte code
-// pieces and scale bytes of a row meet in one L2 before write-back.
+// Workgroups: 8 waves on 8 consecutive blocks and the same NT token tiles, so
+// one workgroup reads 512 contiguous bytes per row; each wave builds its
+// block's A fragments once and reuses them for its NT tiles.  The waves leave
+// their code and scale bytes in LDS, and after one barrier the workgroup
+// writes each row's 128 bytes of codes with 8 lanes x 16 bytes and its 8
+// scale bytes with one 8-byte store: scattered 8-byte and 1-byte stores from
+// the accumulator layout cost more than the whole read stream.  The
+// workgroup index is mapped so that all block groups of a tile range run on
+// the same XCD (workgroups go to the 8 XCDs round-robin), so the 8-byte scale
+// pieces of a row meet in one L2.
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -36,7 +42,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMfmaThreads = 256;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kXcds = 8;
 
 // Value of lane l^32's v in every lane (v_permlane32_swap exchanges the
@@ -63,28 +70,31 @@ template <int NT>
 __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t ld, const float *__restrict__ lu,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int tokens, int nb, int tiles,
-    int ntg) {
-    // Workgroup -> (tile group, block), all blocks of a tile group on one XCD.
+    int nranges, int ngroups) {
+    // Workgroup -> (tile range, block group); every block group of a tile
+    // range on the same XCD.
     const int b = blockIdx.x;
     const int slot = b / kXcds;
-    const int j = slot % nb;
-    const int tg = (slot / nb) * kXcds + b % kXcds;
-    if (tg >= ntg) return;
+    const int grp = slot % ngroups;
+    const int range = (slot / ngroups) * kXcds + b % kXcds;
+    if (range >= nranges) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Waves past the last block stay for the barrier and compute a copy of
+    // the last block, which is never stored.
+    const int jw = grp * kMfmaWaves + wave;
+    const int j = jw < nb ? jw : nb - 1;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, n = lane & 31;
     const int64_t d = (int64_t)nb * 32;
 
     // ---- all loads first: this wave's NT tiles, two 16-byte pieces each ----
     u32x4 xb[NT][2];
-    int rows[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-        int tile = tg * 4 * NT + wave + 4 * k;
+        int tile = range * NT + k;
         tile = tile < tiles ? tile : tiles - 1;
         int row = tile * 32 + n;
         row = row < tokens ? row : tokens - 1;
-        rows[k] = row;
         const u32x4 *p = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ld + (int64_t)j * 32 + 8 * h);
         xb[k][0] = p[0];  // input channels 8h .. 8h+7
         xb[k][1] = p[2];  // input channels 16 + 8h .. 16 + 8h + 7
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
 #pragma unroll
     for (int bb = 0; bb < 5; ++bb) {
         const float l_ = p[3 * bb], u = p[3 * bb + 1], v = p[3 * bb + 2];
-        const float f00 = u, f01 = v, f10 = l_ * u, f11 = __builtin_fmaf(l_, v, 1.0f / u);
+        const float f00 = u, f01 = v, f10 = l_ * u, f11 = __builtin_fmaf(l_, v, rcp_rn(u));
         const bool kb = (n >> bb) & 1;
         r0[bb] = kb ? f01 : f00;
         r1[bb] = kb ? f11 : f10;
@@ -117,7 +127,14 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
         }
     }
 
-    // ---- per tile: 6 MFMAs, then amax / scale / convert / store ----
+    // Staged outputs: codes [NT][32 rows][136 B] (128 B + pad: 34-dword row
+    // stride keeps the 8-byte writes of 32 rows on distinct banks), scales
+    // [NT][32][8].
+    __shared__ uint64_t lds_codes[NT][32][17];
+    __shared__ uint64_t lds_scales[NT][32];
+    uint8_t *lsc = reinterpret_cast<uint8_t *>(lds_scales);
+
+    // ---- per tile: 6 MFMAs, then amax / scale / convert / stage ----
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
         f32x16 acc = {};
@@ -136,8 +153,8 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
         float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
 #pragma unroll
         for (int r = 2; r < 16; r += 2)
-            m = __builtin_elementwise_maximum(
-                m, __builtin_elementwise_maximum(__builtin_fabsf(y[r]), __builtin_fabsf(y[r + 1])));
+            m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(y[r])),
+                                              __builtin_fabsf(y[r + 1]));
         const float mo = __uint_as_float(swap_halves(__float_as_uint(m), h));
         const float amax = __builtin_elementwise_maximum(m, mo);
         const uint32_t s = e8m0_from_amax(amax);
@@ -150,21 +167,48 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
         uint32_t d0 = (lo & 0xffffu) | (hi << 16);
         uint32_t d1 = (lo >> 16) | (hi & 0xffff0000u);
         if (s == 255u) d0 = d1 = 0u;
-        const int64_t row = rows[k];
-        __builtin_nontemporal_store(u32x2{d0, d1},
-                                    reinterpret_cast<u32x2 *>(codes + row * (d / 2) + (int64_t)j * 16 + 8 * h));
-        __builtin_nontemporal_store((uint8_t)s, scales + row * nb + j);
+        lds_codes[k][n][2 * wave + h] = (uint64_t)d0 | ((uint64_t)d1 << 32);
+        if (h == 0) lsc[(k * 32 + n) * 8 + wave] = (uint8_t)s;
+    }
+    __syncthreads();
+
+    // ---- cooperative stores: 16 B per lane, 8 lanes per 128-byte row ----
+    const int nblk = nb - grp * kMfmaWaves < kMfmaWaves ? nb - grp * kMfmaWaves : kMfmaWaves;
+    for (int c = threadIdx.x; c < NT * 32 * 8; c += kMfmaThreads) {
+        const int k = c >> 8, r = (c >> 3) & 31, q = c & 7;
+        if (q >= nblk) continue;
+        int tile = range * NT + k;
+        tile = tile < tiles ? tile : tiles - 1;
+        int row = tile * 32 + r;
+        row = row < tokens ? row : tokens - 1;
+        const uint64_t a0 = lds_codes[k][r][2 * q], a1 = lds_codes[k][r][2 * q + 1];
+        __builtin_nontemporal_store(
+            u32x4{(uint32_t)a0, (uint32_t)(a0 >> 32), (uint32_t)a1, (uint32_t)(a1 >> 32)},
+            reinterpret_cast<u32x4 *>(codes + (int64_t)row * (d / 2) + (int64_t)(grp * kMfmaWaves + q) * 16));
+    }
+    for (int c = threadIdx.x; c < NT * 32; c += kMfmaThreads) {
+        const int k = c >> 5, r = c & 31;
+        int tile = range * NT + k;
+        tile = tile < tiles ? tile : tiles - 1;
+        int row = tile * 32 + r;
+        row = row < tokens ? row : tokens - 1;
+        uint8_t *dst = scales + (int64_t)row * nb + grp * kMfmaWaves;
+        if (nblk == kMfmaWaves && ((uintptr_t)dst & 7) == 0) {
+            *reinterpret_cast<uint64_t *>(dst) = lds_scales[k][r];  // partial line: plain store
+        } else {
+            for (int q = 0; q < nblk; ++q) dst[q] = lsc[c * 8 + q];
+        }
     }
 }
 
 static int mfma_tiles_per_wave() {
     static int cached = 0;
     if (cached == 0) {
-        int v = 2;
+        int v = 4;
         const char *e = getenv("KQ_MFMA_TILES_PER_WAVE");
         if (e) {
             int q = atoi(e);
-            if (q == 1 || q == 2 || q == 4) v = q;
+            if (q == 1 || q == 2 || q == 4 || q == 8) v = q;
         }
         cached = v;
     }
@@ -187,17 +231,18 @@ extern "C" kq_status kq_transform_quant_mfma(const void *x, int64_t tokens, int6
     const int nb = (int)(d / 32);
     const int tiles = (int)((tokens + 31) / 32);
     const int nt = mfma_tiles_per_wave();
-    const int per_wg = 4 * nt;
-    const int ntg = (tiles + per_wg - 1) / per_wg;
-    const int64_t grid = (int64_t)((ntg + kXcds - 1) / kXcds) * kXcds * nb;
+    const int nranges = (tiles + nt - 1) / nt;
+    const int ngroups = (nb + kMfmaWaves - 1) / kMfmaWaves;
+    const int64_t grid = (int64_t)((nranges + kXcds - 1) / kXcds) * kXcds * ngroups;
     if (grid > INT32_MAX) return KQ_ERR_SHAPE;
     const uint16_t *xp = (const uint16_t *)x;
     const int t = (int)tokens;
     void *args[] = {(void *)&xp, (void *)&ld_x, (void *)&lu, (void *)&codes, (void *)&scales,
-                    (void *)&t, (void *)&nb, (void *)&tiles, (void *)&ntg};
+                    (void *)&t, (void *)&nb, (void *)&tiles, (void *)&nranges, (void *)&ngroups};
     const void *fn = nt == 1 ? (const void *)kron_mfma_kernel<1>
-                   : nt == 4 ? (const void *)kron_mfma_kernel<4>
-                             : (const void *)kron_mfma_kernel<2>;
+                   : nt == 2 ? (const void *)kron_mfma_kernel<2>
+                   : nt == 8 ? (const void *)kron_mfma_kernel<8>
+                             : (const void *)kron_mfma_kernel<4>;
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kMfmaThreads), args, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;

@@ -94,7 +94,7 @@ struct KronStage {
             l[b] = p[3 * b + 0];
             u[b] = p[3 * b + 1];
             w[b] = u[b] * p[3 * b + 2];
-            iu[b] = 1.0f / u[b];  // IEEE division (correctly rounded)
+            iu[b] = rcp_rn(u[b]);  // = IEEE 1/u
         }
         // d_k as the running product over b = 0..4, built bit by bit.
         dk[0] = u[0];
