@@ -57,6 +57,108 @@ def load_traffic(kernel: str, workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+KERNEL_MATCH = {
+    "kq_transform_quant": "KronStage, kq::Mxfp4Sink",
+    "kq_transform_quant_mfma": "kron_mfma_kernel",
+    "kq_smooth_quant": "SmoothStage, kq::Mxfp4Sink",
+    "kq_fwht32_quant": "FwhtStage, kq::Mxfp4Sink",
+    "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
+}
+
+PROFILE_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp; cd $REPO
+rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o trace -- python3 bench.py --steps 200 --warmup 50 --no-cpu
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o FETCH_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/WRITE_SIZE -o WRITE_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration --steps 20
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration --steps 20
+python3 bench.py --summarize-profiles OUT"""
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(directory, suffix):
+    for root, _, files in os.walk(directory):
+        for name in files:
+            if name.endswith(suffix):
+                return os.path.join(root, name)
+    raise FileNotFoundError(f"no *{suffix} under {directory}")
+
+
+def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
+    """Turn the rocprofv3 CSV outputs of PROFILE_COMMANDS into the short
+    summaries kept under profiles/ (kernel durations; HBM bytes per launch
+    from FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads
+    for a device-to-device copy of 64 MiB)."""
+    from mxfp4_activation_quantizer_amd import inputs
+    w = inputs.WORKLOADS[workload]
+    nbytes = w.algorithmic_bytes
+    os.makedirs(PROFILES, exist_ok=True)
+    src_hash = kernel_source_hash()
+
+    stats = _csv_rows(_find(os.path.join(out_dir, "trace"), "kernel_stats.csv"))
+    lines = [f"# rocprofv3 --kernel-trace --stats, {workload} {w.tokens}x{w.d} bf16, one MI355X",
+             f"# kernel sources {src_hash}; commands (REPO = repository root, OUT = output dir):"]
+    lines += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    lines.append(f"# algorithmic bytes per launch: {nbytes}")
+    lines.append(f"{'entry point':26s} {'calls':>6s} {'avg us':>8s} {'min us':>8s} "
+                 f"{'max us':>8s} {'GB/s(avg)':>10s}")
+    for entry, key in KERNEL_MATCH.items():
+        for r in stats:
+            if key in r["Name"]:
+                avg = float(r["AverageNs"]) / 1e3
+                lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
+                             f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} "
+                             f"{nbytes / (avg * 1e3):10.1f}")
+    with open(os.path.join(PROFILES, f"kernel_stats_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def counter_avg(sub, counter, match):
+        rows = _csv_rows(_find(os.path.join(out_dir, sub), "counter_collection.csv"))
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+        if not vals:
+            raise ValueError(f"{counter}: no dispatch matching {match!r} in {sub}")
+        return sum(vals) / len(vals), len(vals)
+
+    copy_kib = (64 << 20) / 1024
+    cf, ncf = counter_avg("copy_FETCH_SIZE", "FETCH_SIZE", "copyBuffer")
+    cw, ncw = counter_avg("copy_WRITE_SIZE", "WRITE_SIZE", "copyBuffer")
+    kf, nkf = counter_avg("FETCH_SIZE", "FETCH_SIZE", KERNEL_MATCH["kq_transform_quant"])
+    kw, nkw = counter_avg("WRITE_SIZE", "WRITE_SIZE", KERNEL_MATCH["kq_transform_quant"])
+    fs, ws = copy_kib / cf, copy_kib / cw
+    read_b, write_b = kf * fs * 1024, kw * ws * 1024
+    rec = {"kernel": "kq_transform_quant", "workload": workload, "source_hash": src_hash,
+           "fetch_size_kib": round(kf, 2), "write_size_kib": round(kw, 2),
+           "copy_fetch_size_kib": round(cf, 2), "copy_write_size_kib": round(cw, 2),
+           "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+           "hbm_read_bytes_per_launch": round(read_b), "hbm_write_bytes_per_launch": round(write_b),
+           "hbm_bytes_per_launch": round(read_b + write_b),
+           "algorithmic_bytes_per_launch": nbytes,
+           "traffic_over_algorithmic": round((read_b + write_b) / nbytes, 4),
+           "dispatches": {"kernel_fetch": nkf, "kernel_write": nkw, "copy_fetch": ncf,
+                          "copy_write": ncw}}
+    with open(os.path.join(PROFILES, f"traffic_kq_transform_quant_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    txt = [f"# HBM traffic of kq_transform_quant, {workload} {w.tokens}x{w.d}, from rocprofv3 --pmc",
+           f"# kernel sources {src_hash}; commands:"]
+    txt += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    txt += [f"FETCH_SIZE per dispatch   {kf:12.1f} KiB (x{fs:.4f} copy scale) = {read_b / 1e6:9.3f} MB",
+            f"WRITE_SIZE per dispatch   {kw:12.1f} KiB (x{ws:.4f} copy scale) = {write_b / 1e6:9.3f} MB",
+            f"64 MiB device copy reads  FETCH_SIZE {cf:10.1f} KiB, WRITE_SIZE {cw:10.1f} KiB",
+            f"HBM bytes per launch      {(read_b + write_b) / 1e6:9.3f} MB",
+            f"algorithmic bytes         {nbytes / 1e6:9.3f} MB  (ratio {(read_b + write_b) / nbytes:.4f})"]
+    with open(os.path.join(PROFILES, f"hbm_traffic_kq_transform_quant_{workload}.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(lines + txt))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,11 +174,15 @@ def main() -> int:
                     choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
                              "kq_fwht32_quant", "kq_copy_ceiling"],
                     help="the entry point --kernel-only times")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="summarise rocprofv3 CSV outputs under DIR into profiles/ and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 64 MiB device-to-device copy, the known-size "
                          "reference for the HBM byte counters")
     args = ap.parse_args()
 
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles, args.workload)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(token rows shard with no exchange; see the design notes). "
@@ -96,7 +202,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         n = 64 << 20
-        srcs = [torch.ones(n // 2, dtype=torch.bfloat16, device=dev) for _ in range(8)]
+        srcs = [torch.empty(n // 2, dtype=torch.bfloat16, device=dev) for _ in range(8)]
         dsts = [torch.empty_like(srcs[0]) for _ in range(8)]
         for i in range(args.steps):
             dsts[i % 8].copy_(srcs[i % 8])

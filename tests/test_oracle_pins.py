@@ -442,3 +442,14 @@ def test_dense64_vs_staged32_codes_within_tie_tolerance(oracle):
     same = np.repeat(s64 == s32, 16, axis=1)
     d = (c64 != c32) & same
     assert d.mean() <= 2e-4   # bytes hold two codes
+
+
+def test_forward_error_scale_closed_form_at_hadamard_start(oracle):
+    """At the Hadamard start |T_ik| = 1/sqrt(32), so sum_i |x_i||T_ik| is
+    sum_i |x_i| / sqrt(32) for every output k."""
+    x = inputs.activation("tiny")
+    lu = inputs.hadamard_init(x.shape[1] // 32)
+    b = oracle.transform_absbound(x, lu)
+    xf = np.abs(inputs.bf16_bits_to_f32(x).astype(np.float64)).reshape(x.shape[0], -1, 32)
+    want = np.repeat(xf.sum(axis=2), 32, axis=1) / np.sqrt(32)
+    np.testing.assert_allclose(b, want, rtol=1e-6)
