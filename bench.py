@@ -63,6 +63,7 @@ KERNEL_MATCH = {
     "kq_smooth_quant": "SmoothStage, kq::Mxfp4Sink",
     "kq_fwht32_quant": "FwhtStage, kq::Mxfp4Sink",
     "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
+    "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
 }
 
 PROFILE_COMMANDS = """\
@@ -172,7 +173,7 @@ def main() -> int:
                     help="run only the timed steps of one kernel (for profilers)")
     ap.add_argument("--kernel", default="kq_transform_quant",
                     choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
-                             "kq_fwht32_quant", "kq_copy_ceiling"],
+                             "kq_fwht32_quant", "kq_copy_ceiling", "kq_dequant_inverse"],
                     help="the entry point --kernel-only times")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise rocprofv3 CSV outputs under DIR into profiles/ and exit")
@@ -236,6 +237,9 @@ def main() -> int:
             xp, cp, scp = xs[i].data_ptr(), codes[i].data_ptr(), scales[i].data_ptr()
             if fn_name in ("kq_transform_quant", "kq_transform_quant_mfma"):
                 out.append((xp, T, d, d, lu_d.data_ptr(), cp, scp, sp))
+            elif fn_name == "kq_dequant_inverse":
+                # codes/scales of set i back to the bf16 buffer of set i
+                out.append((cp, scp, T, d, lu_d.data_ptr(), xp, d, sp))
             elif fn_name == "kq_smooth_quant":
                 out.append((xp, T, d, d, mult_d.data_ptr(), cp, scp, sp))
             else:
@@ -272,7 +276,8 @@ def main() -> int:
         for name, fn_name in [("transform_quant_mfma", "kq_transform_quant_mfma"),
                               ("smooth_quant", "kq_smooth_quant"),
                               ("fwht32_quant", "kq_fwht32_quant"),
-                              ("copy_ceiling", "kq_copy_ceiling")]:
+                              ("copy_ceiling", "kq_copy_ceiling"),
+                              ("dequant_inverse", "kq_dequant_inverse")]:
             pms = timed(fn_name, args.steps, args.warmup)
             extra[name] = {"ms_per_step": round(pms, 6),
                            "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}

@@ -144,6 +144,27 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
                              uint8_t *codes, uint8_t *scales, void *stream);
 
 /*
+ * kq_dequant_inverse — the inverse side: decode MXFP4 and undo the block
+ * transform, x = dequant(codes, scales) * T_j^-1, rounded to bf16 (nearest
+ * even).  The transform is invertible with unit determinant (KroQuant
+ * summary, "Approach"; abstract: "applies an invertible linear transform to
+ * the activations and its inverse to the weights").
+ *
+ *   codes   uint8 [tokens][d/2], 16-byte aligned (layout as above)
+ *   scales  uint8 [tokens][d/32]
+ *   lu      fp32 [d/32][5][3], the parameters that produced the codes
+ *   x_out   bf16 [tokens][ld_out], 16-byte aligned, ld_out % 8 == 0 (written)
+ *
+ * Fixed fp32 order: the decoded value is code value * 2^(s-127) (exact; a
+ * 0xFF scale makes the whole block NaN); then z_k = y_k * e_k, e_k the
+ * left-to-right product over b = 0..4 of (bit b of k ? u_b : 1/u_b); then bits
+ * b = 4..0 map each pair (r, s) to q = fma(-w_b, r, s), p = fma(-l_b, q, r).
+ */
+kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
+                             int64_t d, const float *lu, void *x_out, int64_t ld_out,
+                             void *stream);
+
+/*
  * kq_copy_ceiling — not a quantizer: moves the same bytes as
  * kq_transform_quant (reads the bf16 tensor, writes d/2 + d/32 bytes per row)
  * with almost no arithmetic, to measure the achievable bandwidth of this

@@ -68,6 +68,39 @@ struct F32Src {
     }
 };
 
+// MXFP4 input (the inverse side): 16 code bytes + 1 scale byte per unit,
+// decoded by the gfx950 scaled convert (code value times 2^(s-127)); a NaN
+// scale byte makes the whole block NaN.
+struct Mxfp4Src {
+    const uint8_t *codes;   // [tokens][d/2]
+    const uint8_t *scales;  // [tokens][nb]
+    int nb;
+    struct Raw { u32x4 c; uint32_t s; };
+    __device__ __forceinline__ void load(int t, int j, Raw &r) const {
+        const int64_t unit = (int64_t)t * nb + j;
+        r.c = reinterpret_cast<const u32x4 *>(codes)[unit];
+        r.s = scales[unit];
+    }
+    __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
+        const float scale = __uint_as_float(r.s << 23);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 0);
+            const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 1);
+            const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 2);
+            const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 3);
+            z[8 * q + 0] = v0[0]; z[8 * q + 1] = v0[1];
+            z[8 * q + 2] = v1[0]; z[8 * q + 3] = v1[1];
+            z[8 * q + 4] = v2[0]; z[8 * q + 5] = v2[1];
+            z[8 * q + 6] = v3[0]; z[8 * q + 7] = v3[1];
+        }
+        if (r.s == 255u) {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) z[k] = __builtin_nanf("");
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Transform stages.
 // ---------------------------------------------------------------------------
@@ -124,6 +157,60 @@ struct KronStage {
         }
 #pragma unroll
         for (int k = 0; k < 32; ++k) z[k] = z[k] * dk[k];
+    }
+};
+
+// Inverse of the block transform: T^-1 = (D_4 (x)...(x) D_0)^-1 (G_4 (x)...(x) G_0)^-1
+// (the inverse of y = x * T, KroQuant abstract: "invertible" transform, its
+// inverse applied to the weights).  First z_k = y_k * e_k with e_k the running
+// product over b = 0..4 of (bit b of k ? u_b : 1/u_b); then bits b = 4..0 map
+// each pair (r, s) back by q = s - w*r, p = r - l*q (two fused multiply-adds).
+struct KronInverseStage {
+    const float *lu;
+    float p[15];
+    float l[5], w[5], ek[32];
+    __device__ __forceinline__ void fetch(int j) {
+        const float *src = lu + (int64_t)j * 15;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) p[i] = src[i];
+    }
+    __device__ __forceinline__ void setup() {
+        float u[5], iu[5];
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            l[b] = p[3 * b + 0];
+            u[b] = p[3 * b + 1];
+            w[b] = u[b] * p[3 * b + 2];
+            iu[b] = rcp_rn(u[b]);
+        }
+        ek[0] = iu[0];
+        ek[1] = u[0];
+#pragma unroll
+        for (int b = 1; b < 5; ++b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int k = 0; k < h; ++k) {
+                ek[k + h] = ek[k] * u[b];
+                ek[k] = ek[k] * iu[b];
+            }
+        }
+    }
+    __device__ __forceinline__ void apply(float (&z)[32]) const {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = z[k] * ek[k];
+#pragma unroll
+        for (int b = 4; b >= 0; --b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h) continue;
+                const float r = z[i], s = z[i | h];
+                const float q = __builtin_fmaf(-w[b], r, s);
+                const float pv = __builtin_fmaf(-l[b], q, r);
+                z[i] = pv;
+                z[i | h] = q;
+            }
+        }
     }
 };
 
@@ -190,6 +277,22 @@ struct Mxfp4Sink {
         const int64_t unit = (int64_t)t * nb + j;
         __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(codes) + unit);
         __builtin_nontemporal_store((uint8_t)s, scales + unit);
+    }
+};
+
+// bf16 output, rounded to nearest even by the hardware pack-convert.
+struct Bf16Sink {
+    uint16_t *x;  // [tokens][ld]
+    int64_t ld;
+    __device__ __forceinline__ void store(int t, int j, const float (&z)[32]) const {
+        uint32_t w[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            w[m] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector(f32x2{z[2 * m], z[2 * m + 1]}, bf16x2));
+        u32x4 *p = reinterpret_cast<u32x4 *>(x + (int64_t)t * ld + (int64_t)j * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
     }
 };
 
@@ -438,6 +541,19 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
     if (!aligned(y, 16) || (ld_y * 4) % 16 != 0) return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
     return run(F32Src{y, ld_y}, IdentityStage{}, Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+}
+
+kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
+                             int64_t d, const float *lu, void *x_out, int64_t ld_out,
+                             void *stream) {
+    kq_status st = check_shape(tokens, d, ld_out);
+    if (st != KQ_OK || tokens == 0) return st;
+    if (!codes || !scales || !lu || !x_out) return KQ_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(x_out, 16) || (ld_out * 2) % 16 != 0 || !aligned(lu, 4))
+        return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    return run(Mxfp4Src{codes, scales, nb}, KronInverseStage{lu, {}, {}, {}, {}},
+               Bf16Sink{(uint16_t *)x_out, ld_out}, tokens, nb, stream);
 }
 
 kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x,

@@ -37,6 +37,7 @@ SIGNATURES = {
     "kq_smooth_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_fwht32_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kq_mxfp4_quant_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_dequant_inverse": (_ST, [_P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -105,6 +106,10 @@ def kq_fwht32_quant(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
 
 def kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream=None) -> int:
     return lib().kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream)
+
+
+def kq_dequant_inverse(codes, scales, tokens, d, lu, x_out, ld_out, stream=None) -> int:
+    return lib().kq_dequant_inverse(codes, scales, tokens, d, lu, x_out, ld_out, stream)
 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
@@ -214,3 +219,17 @@ def copy_ceiling(x, d: int | None = None, codes=None, scales=None):
     _check("kq_copy_ceiling", kq_copy_ceiling(
         x.data_ptr(), tokens, d, ld, codes.data_ptr(), scales.data_ptr(), _stream(x)))
     return codes, scales
+
+
+def dequant_inverse(codes, scales, lu, x_out=None):
+    """bf16 [tokens][d] = dequant(codes, scales) times the inverse block transform."""
+    torch = _torch()
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or not codes.is_cuda:
+        raise ValueError("codes must be a 2-D uint8 GPU tensor")
+    tokens, d = codes.shape[0], codes.shape[1] * 2
+    if x_out is None:
+        x_out = torch.empty((tokens, d), dtype=torch.bfloat16, device=codes.device)
+    _check("kq_dequant_inverse", kq_dequant_inverse(
+        codes.data_ptr(), scales.data_ptr(), tokens, d, lu.data_ptr(), x_out.data_ptr(),
+        x_out.stride(0), _stream(codes)))
+    return x_out

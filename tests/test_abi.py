@@ -86,6 +86,15 @@ def test_parameter_pointer_checks():
     assert kq.kq_mxfp4_quant_f32(A16, 4, 64, 60, A16, A16) == kq.KQ_ERR_SHAPE
     assert kq.kq_mxfp4_quant_f32(None, 4, 64, 64, A16, A16) == kq.KQ_ERR_NULL
     assert kq.kq_mxfp4_quant_f32(None, 0, 64, 64, None, None) == kq.KQ_OK
+    di = kq.kq_dequant_inverse
+    assert di(None, None, 0, 64, None, None, 64) == kq.KQ_OK
+    assert di(A16, A16, 4, 48, A16, A16, 64) == kq.KQ_ERR_SHAPE
+    assert di(A16, A16, 4, 64, A16, A16, 32) == kq.KQ_ERR_SHAPE
+    assert di(A16, None, 4, 64, A16, A16, 64) == kq.KQ_ERR_NULL
+    assert di(A16, A16, 4, 64, None, A16, 64) == kq.KQ_ERR_NULL
+    assert di(ODD, A16, 4, 64, A16, A16, 64) == kq.KQ_ERR_ALIGN
+    assert di(A16, A16, 4, 64, A16, ODD, 64) == kq.KQ_ERR_ALIGN
+    assert di(A16, A16, 4, 64, A16, A16, 68) == kq.KQ_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -419,3 +419,106 @@ def test_mfma_full_size_workload_sampled(torch_cuda, name):
     bc, bs = _gpu_tq(x, lu)
     assert np.mean(bs != s) < 1e-4
     assert np.mean(bc != c) < 2e-4
+
+
+# --------------------------------------------------------------------------
+# the inverse side: dequantise and undo the transform
+# --------------------------------------------------------------------------
+def _bf16_equal_or_both_nan(a, b):
+    af, bf = inputs.bf16_bits_to_f32(a), inputs.bf16_bits_to_f32(b)
+    both_nan = np.isnan(af) & np.isnan(bf)
+    return (a == b) | both_nan
+
+
+def _gpu_dequant_inverse(codes, scales, lu):
+    torch = __import__("torch")
+    out = kq.dequant_inverse(to_gpu(codes), to_gpu(scales), to_gpu(lu))
+    return _np(out.view(torch.int16)).view(np.uint16)
+
+
+def test_dequant_inverse_every_code_and_scale(torch_cuda):
+    """All 16 codes in both nibbles under all 256 scale bytes (0xFF = NaN
+    block), random parameters: bit-exact with the oracle's fixed order."""
+    g = np.random.default_rng(11)
+    tokens, nb = 256, 4
+    codes = g.integers(0, 256, (tokens, nb * 16), dtype=np.uint8)
+    scales = np.tile(np.arange(256, dtype=np.uint8)[:, None], (1, nb))
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.1, (nb, 5, 3))).astype(np.float32)
+    got = _gpu_dequant_inverse(codes, scales, lu)
+    want = oracle.dequant_inverse(codes, scales, lu, oracle.STAGED32)
+    assert np.all(_bf16_equal_or_both_nan(got, want))
+    assert np.isnan(inputs.bf16_bits_to_f32(got[255])).all()
+
+
+def test_dequant_inverse_identity_is_plain_decode(torch_cuda):
+    g = np.random.default_rng(12)
+    codes = g.integers(0, 256, (64, 128), dtype=np.uint8)
+    scales = g.integers(100, 150, (64, 8), dtype=np.uint8)
+    lu = np.tile(IDENTITY, (8, 5, 1))
+    got = inputs.bf16_bits_to_f32(_gpu_dequant_inverse(codes, scales, lu))
+    want = oracle.mxfp4_dequant(codes, scales)
+    np.testing.assert_array_equal(got, want)
+
+
+def _inverse_vs_definition(codes, scales, lu, got):
+    """bf16 results vs the fp64 inverse: equal, one bf16 step apart, or within
+    1e-5 of sum_i |y_i| |Tinv_ik| (cancellation)."""
+    yh = oracle.mxfp4_dequant(codes, scales).astype(np.float64)
+    nb = codes.shape[1] // 16
+    exact = np.empty_like(yh)
+    bound = np.empty_like(yh)
+    for j in range(nb):
+        Ti = oracle.block_inverse_matrix(lu[j])
+        exact[:, 32 * j:32 * j + 32] = yh[:, 32 * j:32 * j + 32] @ Ti
+        bound[:, 32 * j:32 * j + 32] = np.abs(yh[:, 32 * j:32 * j + 32]) @ np.abs(Ti)
+    g = inputs.bf16_bits_to_f32(got).astype(np.float64)
+    ok = (np.abs(g - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-5 * bound)
+    assert ok.all(), f"{(~ok).sum()} outputs off the fp64 inverse"
+
+
+def test_dequant_inverse_round_trip_tiny(torch_cuda):
+    x, lu = inputs.activation("tiny"), inputs.lu_params("tiny")
+    c, s = _gpu_tq(x, lu)
+    got = _gpu_dequant_inverse(c, s, lu)
+    want = oracle.dequant_inverse(c, s, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(got, want)
+    _inverse_vs_definition(c, s, lu, got)
+
+
+@pytest.mark.parametrize("tokens,nb", [(1, 1), (77, 3), (129, 36), (33, 97)])
+def test_dequant_inverse_ragged(torch_cuda, tokens, nb):
+    g = np.random.default_rng(tokens + 7 * nb)
+    x = inputs.f64_to_bf16_bits(g.standard_normal((tokens, nb * 32)) * 3)
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    c, s = _gpu_tq(x, lu)
+    got = _gpu_dequant_inverse(c, s, lu)
+    np.testing.assert_array_equal(got, oracle.dequant_inverse(c, s, lu, oracle.STAGED32))
+    _inverse_vs_definition(c, s, lu, got)
+
+
+def test_round_trip_error_flux_mlp(torch_cuda):
+    """FLUX-MLP-shaped input: quantise then dequantise+invert on the GPU; the
+    relative Frobenius error of the Kron path is reported next to the
+    per-channel-scaling and FWHT32 round trips (oracle, sampled rows)."""
+    x = inputs.activation("flux_mlp")
+    lu = inputs.lu_params("flux_mlp")
+    c, s = _gpu_tq(x, lu)
+    xr = inputs.bf16_bits_to_f32(_gpu_dequant_inverse(c, s, lu)).astype(np.float64)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    err_kron = np.linalg.norm(xr - xf) / np.linalg.norm(xf)
+    rows = np.random.default_rng(3).choice(x.shape[0], 64, replace=False)
+    xs = x[rows]
+    m = inputs.smooth_multipliers(x)
+    sc, ss = oracle.smooth_quant(xs, m)
+    xs_s = oracle.mxfp4_dequant(sc, ss).astype(np.float64) / m[None, :]
+    fc, fs = oracle.fwht32_quant(xs, oracle.DENSE64)
+    yh = oracle.mxfp4_dequant(fc, fs).astype(np.float64)
+    import scipy.linalg
+    H = scipy.linalg.hadamard(32) / np.sqrt(32)
+    xs_f = np.concatenate([yh[:, 32 * j:32 * j + 32] @ H for j in range(x.shape[1] // 32)], 1)
+    xsf = inputs.bf16_bits_to_f32(xs).astype(np.float64)
+    err_s = np.linalg.norm(xs_s - xsf) / np.linalg.norm(xsf)
+    err_f = np.linalg.norm(xs_f - xsf) / np.linalg.norm(xsf)
+    _log(f"round-trip rel. Frobenius error, FLUX-MLP: kron {err_kron:.4f}, "
+         f"smooth {err_s:.4f}, fwht32 {err_f:.4f}")
+    assert np.isfinite(err_kron) and err_kron < 0.5
