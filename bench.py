@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak
 MALL_BYTES = 256 << 20         # Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
@@ -64,6 +65,8 @@ KERNEL_MATCH = {
     "kq_fwht32_quant": "FwhtStage, kq::Mxfp4Sink",
     "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
+    "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
+    "kq_w4a4_gemm": "w4a4_gemm_kernel",
 }
 
 PROFILE_COMMANDS = """\
@@ -173,7 +176,8 @@ def main() -> int:
                     help="run only the timed steps of one kernel (for profilers)")
     ap.add_argument("--kernel", default="kq_transform_quant",
                     choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
-                             "kq_fwht32_quant", "kq_copy_ceiling", "kq_dequant_inverse"],
+                             "kq_fwht32_quant", "kq_copy_ceiling", "kq_dequant_inverse",
+                             "kq_weight_quant", "kq_w4a4_gemm"],
                     help="the entry point --kernel-only times")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise rocprofv3 CSV outputs under DIR into profiles/ and exit")
@@ -231,8 +235,42 @@ def main() -> int:
     sp = stream.cuda_stream
     L = kq.lib()
 
+    # The consumer of the quantized activation: Y = A W^T with MXFP4 A (the
+    # kernel's output) and W (12288 x 3072 prepared by kq_weight_quant).
+    gemm = {}
+    want_gemm = args.kernel in ("kq_w4a4_gemm", "kq_weight_quant") if args.kernel_only \
+        else not args.no_peers
+    if want_gemm and d != inputs.GEMM_K:
+        if args.kernel_only:
+            print(f"the W4A4 consumer takes K = {inputs.GEMM_K} channels", file=sys.stderr)
+            return 2
+        want_gemm = False
+    if want_gemm:
+        wn, wk = inputs.GEMM_N, inputs.GEMM_K
+        gemm["w"] = torch.from_numpy(inputs.gemm_weight().view(np.int16)).view(torch.bfloat16).to(dev)
+        gemm["wc"] = torch.empty((wn, wk // 2), dtype=torch.uint8, device=dev)
+        gemm["ws"] = torch.empty((wn, wk // 32), dtype=torch.uint8, device=dev)
+        gemm["y"] = [torch.empty((T, wn), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        gemm["lu"] = lu_d
+        st = L.kq_weight_quant(gemm["w"].data_ptr(), wn, wk, wk, gemm["lu"].data_ptr(),
+                               gemm["wc"].data_ptr(), gemm["ws"].data_ptr(), sp)
+        if st != 0:
+            raise kq.KQError("kq_weight_quant", st)
+        gemm.update(n=wn, k=wk, flops=2.0 * T * wn * wk,
+                    weight_bytes=wn * wk * (2 + 0.5 + 1 / 32))
+
     def argsets(fn_name):
         out = []
+        if fn_name == "kq_w4a4_gemm":
+            for i in range(R):  # A: the quantized activations of set i
+                y = gemm["y"][i % 2]
+                out.append((codes[i].data_ptr(), scales[i].data_ptr(), gemm["wc"].data_ptr(),
+                            gemm["ws"].data_ptr(), T, gemm["n"], gemm["k"], y.data_ptr(),
+                            gemm["n"], sp))
+            return out
+        if fn_name == "kq_weight_quant":
+            return [(gemm["w"].data_ptr(), gemm["n"], gemm["k"], gemm["k"], gemm["lu"].data_ptr(),
+                     gemm["wc"].data_ptr(), gemm["ws"].data_ptr(), sp)]
         for i in range(R):
             xp, cp, scp = xs[i].data_ptr(), codes[i].data_ptr(), scales[i].data_ptr()
             if fn_name in ("kq_transform_quant", "kq_transform_quant_mfma"):
@@ -249,8 +287,9 @@ def main() -> int:
     def timed(fn_name, steps, warmup):
         fn = getattr(L, fn_name)
         a = argsets(fn_name)
+        n_a = len(a)
         for i in range(warmup):
-            st = fn(*a[i % R])
+            st = fn(*a[i % n_a])
             if st != 0:
                 raise kq.KQError(fn_name, st)
         torch.cuda.synchronize()
@@ -258,15 +297,23 @@ def main() -> int:
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(steps):
-            fn(*a[i % R])
+            fn(*a[i % n_a])
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps  # ms per launch
 
     if args.kernel_only:
+        if args.kernel in ("kq_dequant_inverse", "kq_w4a4_gemm"):
+            timed("kq_transform_quant", R, 0)  # they read the quantizer's outputs
         ms = timed(args.kernel, args.steps, args.warmup)
-        print(json.dumps({"kernel": args.kernel, "ms_per_step": ms,
-                          "GBps": nbytes / (ms * 1e-3) / 1e9}), flush=True)
+        rec = {"kernel": args.kernel, "ms_per_step": ms}
+        if args.kernel == "kq_w4a4_gemm":
+            rec["TFLOPs"] = gemm["flops"] / (ms * 1e-3) / 1e12
+        elif args.kernel == "kq_weight_quant":
+            rec["GBps"] = gemm["weight_bytes"] / (ms * 1e-3) / 1e9
+        else:
+            rec["GBps"] = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps(rec), flush=True)
         return 0
     ms = timed("kq_transform_quant", args.steps, args.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -282,6 +329,16 @@ def main() -> int:
             extra[name] = {"ms_per_step": round(pms, 6),
                            "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+    if gemm:
+        timed("kq_transform_quant", R, 0)  # A operands: fresh quantizer outputs
+        pms = timed("kq_weight_quant", max(10, args.steps // 10), max(2, args.warmup // 10))
+        extra["weight_quant"] = {"ms_per_step": round(pms, 6), "shape": [gemm["n"], gemm["k"]],
+                                 "GBps": round(gemm["weight_bytes"] / (pms * 1e-3) / 1e9, 1)}
+        pms = timed("kq_w4a4_gemm", max(10, args.steps // 10), max(2, args.warmup // 10))
+        tf = gemm["flops"] / (pms * 1e-3) / 1e12
+        extra["w4a4_gemm"] = {"ms_per_step": round(pms, 6), "shape_mnk": [T, gemm["n"], gemm["k"]],
+                              "TFLOPs": round(tf, 1), "peak_TFLOPs": PEAK_FP4_TFLOPS,
+                              "frac": round(tf / PEAK_FP4_TFLOPS, 4)}
 
     src_hash = kernel_source_hash()
     traffic = load_traffic("kq_transform_quant", args.workload, src_hash)

@@ -144,6 +144,25 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
                              uint8_t *codes, uint8_t *scales, void *stream);
 
 /*
+ * kq_weight_quant — weight preparation for the W4A4 consumer: every
+ * 32-channel block (along K) of every weight row is multiplied by T_j^-T and
+ * the result is quantized to MXFP4 along K, so that
+ * (X T)(W T^-T)^T = X W^T (LRQ-DiT Sec. 3.2 Eq. (2) with an invertible T;
+ * KroQuant abstract: "its inverse to the weights").  Runs once per weight
+ * matrix, offline.
+ *
+ *   w       bf16 [rows = N][ld_w] (row-major, K = k contiguous), as for x
+ *   lu      fp32 [k/32][5][3], the activation side's parameters
+ *   codes   uint8 [rows][k/2], scales uint8 [rows][k/32] (written)
+ *
+ * Fixed fp32 order: for bits b = 0..4 each pair (p, q) maps to
+ * s = fma(-l_b, p, q), r = fma(-w_b, s, p); then y_k = z_k * e_k with e_k the
+ * left-to-right product over b = 0..4 of (bit b of k ? u_b : 1/u_b).
+ */
+kq_status kq_weight_quant(const void *w, int64_t rows, int64_t k, int64_t ld_w,
+                          const float *lu, uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
  * kq_dequant_inverse — the inverse side: decode MXFP4 and undo the block
  * transform, x = dequant(codes, scales) * T_j^-1, rounded to bf16 (nearest
  * even).  The transform is invertible with unit determinant (KroQuant
@@ -163,6 +182,24 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
 kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                              int64_t d, const float *lu, void *x_out, int64_t ld_out,
                              void *stream);
+
+/*
+ * kq_w4a4_gemm — the W4A4 consumer of the quantized activations:
+ * Y = dequant(A) * dequant(W)^T with fp32 accumulation and bf16 output
+ * (nearest even), on the gfx950 block-scaled matrix cores (E2M1 operands,
+ * E8M0 scales).  The pages' setting is W4A4 MXFP4 (KroQuant summary; abstract
+ * "W4A4 (MXFP4e2)"): A from kq_transform_quant, W from kq_weight_quant, so
+ * that Y approximates X * W_original^T (LRQ-DiT Sec. 3.2 Eq. (2)).
+ *
+ *   a_codes uint8 [M][K/2] (16-byte aligned), a_scales uint8 [M][K/32] (4-byte aligned)
+ *   w_codes uint8 [N][K/2] (16-byte aligned), w_scales uint8 [N][K/32] (4-byte aligned)
+ *   y       bf16 [M][ld_y], 16-byte aligned, ld_y % 8 == 0, ld_y >= N (written)
+ *
+ * K % 128 == 0; M and N are arbitrary.  M == 0 or N == 0 returns KQ_OK.
+ */
+kq_status kq_w4a4_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
+                       const uint8_t *w_codes, const uint8_t *w_scales, int64_t M, int64_t N,
+                       int64_t K, void *y, int64_t ld_y, void *stream);
 
 /*
  * kq_copy_ceiling — not a quantizer: moves the same bytes as

@@ -165,7 +165,10 @@ struct KronStage {
 // inverse applied to the weights).  First z_k = y_k * e_k with e_k the running
 // product over b = 0..4 of (bit b of k ? u_b : 1/u_b); then bits b = 4..0 map
 // each pair (r, s) back by q = s - w*r, p = r - l*q (two fused multiply-adds).
-struct KronInverseStage {
+// Constants shared by the inverse and the weight-side stages: l_b, w_b and
+// e_k = running product over b = 0..4 of (bit b of k ? u_b : 1/u_b), the
+// diagonal of (D_4 (x)...(x) D_0)^-1.
+struct KronInvConsts {
     const float *lu;
     float p[15];
     float l[5], w[5], ek[32];
@@ -195,6 +198,9 @@ struct KronInverseStage {
             }
         }
     }
+};
+
+struct KronInverseStage : KronInvConsts {
     __device__ __forceinline__ void apply(float (&z)[32]) const {
 #pragma unroll
         for (int k = 0; k < 32; ++k) z[k] = z[k] * ek[k];
@@ -211,6 +217,31 @@ struct KronInverseStage {
                 z[i | h] = q;
             }
         }
+    }
+};
+
+// Weight side of the invariance (X T)(W T^-T)^T = X W^T (LRQ-DiT Sec. 3.2
+// Eq. (2) with an invertible T; KroQuant abstract: the inverse goes to the
+// weights).  T^-T = (G_4^-T (x)...(x) G_0^-T)(D_4 (x)...(x) D_0)^-1 with
+// G^-T = [[1,-l],[0,1]] [[1,0],[-w,1]]: each pair (p, q) on bit b = 0..4 maps
+// to s = q - l*p, r = p - w*s, then every element is multiplied by e_k.
+struct KronWeightStage : KronInvConsts {
+    __device__ __forceinline__ void apply(float (&z)[32]) const {
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            const int h = 1 << b;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h) continue;
+                const float pv = z[i], q = z[i | h];
+                const float s = __builtin_fmaf(-l[b], pv, q);
+                const float r = __builtin_fmaf(-w[b], s, pv);
+                z[i] = r;
+                z[i | h] = s;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = z[k] * ek[k];
     }
 };
 
@@ -543,6 +574,20 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
     return run(F32Src{y, ld_y}, IdentityStage{}, Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
 }
 
+kq_status kq_weight_quant(const void *w, int64_t rows, int64_t k, int64_t ld_w,
+                          const float *lu, uint8_t *codes, uint8_t *scales, void *stream) {
+    kq_status st = check_bf16_act(w, rows, k, ld_w);
+    if (st != KQ_OK || rows == 0) return st;
+    if (!lu) return KQ_ERR_NULL;
+    if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
+    if (!aligned(lu, 4)) return KQ_ERR_ALIGN;
+    const int nb = (int)(k / 32);
+    KronWeightStage stage;
+    stage.lu = lu;
+    return run(Bf16Src{(const uint16_t *)w, ld_w}, stage, Mxfp4Sink{codes, scales, nb}, rows,
+               nb, stream);
+}
+
 kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                              int64_t d, const float *lu, void *x_out, int64_t ld_out,
                              void *stream) {
@@ -552,7 +597,9 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
     if (!aligned(codes, 16) || !aligned(x_out, 16) || (ld_out * 2) % 16 != 0 || !aligned(lu, 4))
         return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    return run(Mxfp4Src{codes, scales, nb}, KronInverseStage{lu, {}, {}, {}, {}},
+    KronInverseStage stage;
+    stage.lu = lu;
+    return run(Mxfp4Src{codes, scales, nb}, stage,
                Bf16Sink{(uint16_t *)x_out, ld_out}, tokens, nb, stream);
 }
 

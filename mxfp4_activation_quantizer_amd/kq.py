@@ -37,7 +37,9 @@ SIGNATURES = {
     "kq_smooth_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_fwht32_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kq_mxfp4_quant_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_weight_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_dequant_inverse": (_ST, [_P, _P, _I64, _I64, _P, _P, _I64, _P]),
+    "kq_w4a4_gemm": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -108,8 +110,16 @@ def kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream=None) -> int:
     return lib().kq_mxfp4_quant_f32(y, tokens, d, ld_y, codes, scales, stream)
 
 
+def kq_weight_quant(w, rows, k, ld_w, lu, codes, scales, stream=None) -> int:
+    return lib().kq_weight_quant(w, rows, k, ld_w, lu, codes, scales, stream)
+
+
 def kq_dequant_inverse(codes, scales, tokens, d, lu, x_out, ld_out, stream=None) -> int:
     return lib().kq_dequant_inverse(codes, scales, tokens, d, lu, x_out, ld_out, stream)
+
+
+def kq_w4a4_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, ld_y, stream=None) -> int:
+    return lib().kq_w4a4_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, ld_y, stream)
 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
@@ -233,3 +243,26 @@ def dequant_inverse(codes, scales, lu, x_out=None):
         codes.data_ptr(), scales.data_ptr(), tokens, d, lu.data_ptr(), x_out.data_ptr(),
         x_out.stride(0), _stream(codes)))
     return x_out
+
+
+def weight_quant(w, lu, k: int | None = None, codes=None, scales=None):
+    """MXFP4 of W * T^-T (per 32-block along K) for bf16 weights ``w`` [N][>=K]."""
+    rows, ld = _act(w, "bf16")
+    k = w.shape[1] if k is None else k
+    codes, scales = _mxfp4_out(w, rows, k, codes, scales)
+    _check("kq_weight_quant", kq_weight_quant(
+        w.data_ptr(), rows, k, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(), _stream(w)))
+    return codes, scales
+
+
+def w4a4_gemm(a_codes, a_scales, w_codes, w_scales, y=None):
+    """bf16 [M][N] = dequant(A) * dequant(W)^T for MXFP4 A [M][K] and W [N][K]."""
+    torch = _torch()
+    M, N, K = a_codes.shape[0], w_codes.shape[0], a_codes.shape[1] * 2
+    if y is None:  # rows padded to a multiple of 8 elements (16-byte aligned)
+        ld = (N + 7) // 8 * 8
+        y = torch.empty((M, ld), dtype=torch.bfloat16, device=a_codes.device)[:, :N]
+    _check("kq_w4a4_gemm", kq_w4a4_gemm(
+        a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
+        M, N, K, y.data_ptr(), y.stride(0), _stream(a_codes)))
+    return y

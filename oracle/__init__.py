@@ -51,6 +51,10 @@ _SIGS = {
     "kqo_mxfp4_dequant": (_INT, [_P, _P, _I64, _I64, _P]),
     "kqo_dequant_inverse": (_INT, [_P, _P, _I64, _I64, _P, _INT, _P, _INT]),
     "kqo_matmul_nt": (_INT, [_P, _P, _I64, _I64, _I64, _P, _INT]),
+    "kqo_block_weight_dense64": (None, [_P, _P, _P]),
+    "kqo_block_weight_staged32": (None, [_P, _P, _P]),
+    "kqo_weight_transform": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _P, _INT]),
+    "kqo_weight_quant": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _P, _P, _INT]),
 }
 
 _lib = None
@@ -307,3 +311,25 @@ def matmul_nt(A: np.ndarray, W: np.ndarray, threads=None) -> np.ndarray:
     rc = lib().kqo_matmul_nt(_ptr(A), _ptr(W), M, N, K, _ptr(Y), threads or default_threads())
     _check(rc, "kqo_matmul_nt")
     return Y
+
+
+def weight_transform(w_bits, lu, mode=DENSE64, k=None, threads=None) -> np.ndarray:
+    """w * T^-T per 32-channel block of every weight row (fp32 out)."""
+    w_bits, rows, k, ld = _x_args(w_bits, k)
+    lu = _lu_arg(lu, k)
+    y = np.zeros((rows, k), np.float32)
+    rc = lib().kqo_weight_transform(_ptr(w_bits), rows, k, ld, _ptr(lu), mode, _ptr(y),
+                                    threads or default_threads())
+    _check(rc, "kqo_weight_transform")
+    return y
+
+
+def weight_quant(w_bits, lu, mode=STAGED32, k=None, threads=None):
+    w_bits, rows, k, ld = _x_args(w_bits, k)
+    lu = _lu_arg(lu, k)
+    codes = np.zeros((rows, k // 2), np.uint8)
+    scales = np.zeros((rows, k // 32), np.uint8)
+    rc = lib().kqo_weight_quant(_ptr(w_bits), rows, k, ld, _ptr(lu), mode, _ptr(codes),
+                                _ptr(scales), threads or default_threads())
+    _check(rc, "kqo_weight_quant")
+    return codes, scales

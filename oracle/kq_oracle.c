@@ -313,6 +313,53 @@ void kqo_block_inverse_staged32(const float y[32], const float p[15], float x[32
     memcpy(x, z, sizeof z);
 }
 
+void kqo_block_weight_dense64(const float w[32], const float p[15], float y[32]) {
+    double Ti[1024];
+    kqo_block_inverse_matrix(p, Ti);
+    for (int k = 0; k < 32; ++k) {
+        /* y = w * Ti^T: y_k = sum_i w_i * Ti[k][i] */
+        double acc = 0.0;
+        for (int i = 0; i < 32; ++i) acc += (double)w[i] * Ti[k * 32 + i];
+        y[k] = (float)acc;
+    }
+}
+
+/*
+ * Fixed fp32 order of w * T^-T.  With T = (G4 (x)...(x) G0)(D4 (x)...(x) D0):
+ * T^-T = (G4^-T (x)...(x) G0^-T)(D4^-1 (x)...(x) D0^-1), and
+ * G^-T = [[1,-l],[0,1]] * [[1,0],[-w,1]].  A row vector pair (p, q) on bit b
+ * therefore maps to s = q - l*p, then r = p - w*s (two fused multiply-adds),
+ * bits b = 0..4 in turn; then y_k = z_k * e_k with e_k the running product over
+ * b = 0..4 of (bit b of k ? u_b : 1/u_b).
+ */
+void kqo_block_weight_staged32(const float w[32], const float p[15], float y[32]) {
+    float l[5], ww[5], u[5], iu[5];
+    for (int b = 0; b < 5; ++b) {
+        l[b] = p[3 * b + 0];
+        u[b] = p[3 * b + 1];
+        ww[b] = p[3 * b + 1] * p[3 * b + 2];
+        iu[b] = 1.0f / p[3 * b + 1];
+    }
+    float z[32];
+    memcpy(z, w, sizeof z);
+    for (int b = 0; b < 5; ++b) {
+        int h = 1 << b;
+        for (int i = 0; i < 32; ++i) {
+            if (i & h) continue;
+            float pv = z[i], qv = z[i | h];
+            float s = fmaf(-l[b], pv, qv);
+            float r = fmaf(-ww[b], s, pv);
+            z[i] = r;
+            z[i | h] = s;
+        }
+    }
+    for (int k = 0; k < 32; ++k) {
+        float ek = (k & 1) ? u[0] : iu[0];
+        for (int b = 1; b < 5; ++b) ek = ek * (((k >> b) & 1) ? u[b] : iu[b]);
+        y[k] = z[k] * ek;
+    }
+}
+
 /* ======================================================================== */
 /* Row-parallel driver                                                       */
 /* ======================================================================== */
@@ -549,6 +596,48 @@ int kqo_fwht32_quant(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
     if (!x || !codes || !scales || bad_shape(tokens, d, ld)) return -1;
     tq_ctx c = {x, d, ld, NULL, mode, NULL, codes, scales, NULL, NULL};
     parallel_rows(row_fwht_quant, &c, tokens, threads);
+    return 0;
+}
+
+/* ---- weight side ---- */
+static void weight_block(const tq_ctx *c, int64_t t, int64_t j, float yb[32]) {
+    float xb[32];
+    load_block(c, t, j, xb);
+    const float *p = c->lu + j * 15;
+    if (c->mode == KQO_DENSE64)
+        kqo_block_weight_dense64(xb, p, yb);
+    else
+        kqo_block_weight_staged32(xb, p, yb);
+}
+
+static void row_weight(void *vc, int64_t t) {
+    tq_ctx *c = (tq_ctx *)vc;
+    for (int64_t j = 0; j < c->d / 32; ++j) weight_block(c, t, j, c->y + t * c->d + j * 32);
+}
+
+static void row_weight_quant(void *vc, int64_t t) {
+    tq_ctx *c = (tq_ctx *)vc;
+    int64_t nb = c->d / 32;
+    for (int64_t j = 0; j < nb; ++j) {
+        float yb[32];
+        weight_block(c, t, j, yb);
+        kqo_mxfp4_block(yb, c->codes + t * (c->d / 2) + j * 16, c->scales + t * nb + j);
+    }
+}
+
+int kqo_weight_transform(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
+                         const float *lu, int mode, float *y, int threads) {
+    if (!w || !lu || !y || bad_shape(rows, k, ld)) return -1;
+    tq_ctx c = {w, k, ld, lu, mode, y, NULL, NULL, NULL, NULL};
+    parallel_rows(row_weight, &c, rows, threads);
+    return 0;
+}
+
+int kqo_weight_quant(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
+                     const float *lu, int mode, uint8_t *codes, uint8_t *scales, int threads) {
+    if (!w || !lu || !codes || !scales || bad_shape(rows, k, ld)) return -1;
+    tq_ctx c = {w, k, ld, lu, mode, NULL, codes, scales, NULL, NULL};
+    parallel_rows(row_weight_quant, &c, rows, threads);
     return 0;
 }
 

@@ -128,6 +128,19 @@ int kqo_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t token
 int kqo_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                         int64_t d, const float *lu, int mode, uint16_t *x_out,
                         int threads);
+/* Weight side of the invariance (XT)(W T^-T)^T = X W^T ([LRQ] Eq. (2) with
+ * an invertible T; [KQ-abs]: the inverse goes to the weights): every
+ * 32-channel block of every weight row (K axis) is multiplied by T_j^-T, then
+ * quantized to MXFP4 along K.  w bf16 [rows][ld], codes [rows][k/2], scales
+ * [rows][k/32].  DENSE64: the fp64 product with the transposed adjugate
+ * Kronecker inverse.  STAGED32: see kqo_block_weight_staged32(). */
+void kqo_block_weight_dense64(const float w[32], const float p[15], float y[32]);
+void kqo_block_weight_staged32(const float w[32], const float p[15], float y[32]);
+int kqo_weight_transform(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
+                         const float *lu, int mode, float *y, int threads);
+int kqo_weight_quant(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
+                     const float *lu, int mode, uint8_t *codes, uint8_t *scales, int threads);
+
 /* Y[m][n] = sum_k A[m][k] * W[n][k] in fp64 (A, W fp32 row-major). */
 int kqo_matmul_nt(const float *A, const float *W, int64_t M, int64_t N, int64_t K,
                   double *Y, int threads);

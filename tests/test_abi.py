@@ -41,6 +41,7 @@ QUANT_CALLS = {
     "kq_transform_quant_mfma": lambda x, t, d, ld, c, s: kq.kq_transform_quant_mfma(
         x, t, d, ld, A16, c, s),
     "kq_smooth_quant": lambda x, t, d, ld, c, s: kq.kq_smooth_quant(x, t, d, ld, A16, c, s),
+    "kq_weight_quant": lambda x, t, d, ld, c, s: kq.kq_weight_quant(x, t, d, ld, A16, c, s),
     "kq_fwht32_quant": lambda x, t, d, ld, c, s: kq.kq_fwht32_quant(x, t, d, ld, c, s),
     "kq_copy_ceiling": lambda x, t, d, ld, c, s: kq.kq_copy_ceiling(x, t, d, ld, c, s),
 }
@@ -95,6 +96,13 @@ def test_parameter_pointer_checks():
     assert di(ODD, A16, 4, 64, A16, A16, 64) == kq.KQ_ERR_ALIGN
     assert di(A16, A16, 4, 64, A16, ODD, 64) == kq.KQ_ERR_ALIGN
     assert di(A16, A16, 4, 64, A16, A16, 68) == kq.KQ_ERR_ALIGN
+    g = kq.kq_w4a4_gemm
+    assert g(None, None, None, None, 0, 16, 128, None, 16) == kq.KQ_OK
+    assert g(A16, A16, A16, A16, 8, 16, 96, A16, 16) == kq.KQ_ERR_SHAPE     # K % 128
+    assert g(A16, A16, A16, A16, 8, 16, 128, A16, 8) == kq.KQ_ERR_SHAPE     # ld_y < N
+    assert g(A16, A16, None, A16, 8, 16, 128, A16, 16) == kq.KQ_ERR_NULL
+    assert g(A16, A16 + 2, A16, A16, 8, 16, 128, A16, 16) == kq.KQ_ERR_ALIGN
+    assert g(A16, A16, A16, A16, 8, 16, 128, A16 + 2, 16) == kq.KQ_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

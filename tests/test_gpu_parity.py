@@ -522,3 +522,96 @@ def test_round_trip_error_flux_mlp(torch_cuda):
     _log(f"round-trip rel. Frobenius error, FLUX-MLP: kron {err_kron:.4f}, "
          f"smooth {err_s:.4f}, fwht32 {err_f:.4f}")
     assert np.isfinite(err_kron) and err_kron < 0.5
+
+
+# --------------------------------------------------------------------------
+# weight preparation: MXFP4 of W * T^-T along K
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,nb", [(64, 8), (77, 3), (130, 36), (5, 97)])
+def test_weight_quant_bit_exact_and_vs_definition(torch_cuda, rows, nb):
+    g = np.random.default_rng(rows + nb)
+    w = inputs.f64_to_bf16_bits(g.normal(0, 0.02, (rows, nb * 32)))
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.1, (nb, 5, 3))).astype(np.float32)
+    c, s = kq.weight_quant(to_gpu_bf16(w), to_gpu(lu))
+    c, s = _np(c), _np(s)
+    wc, ws = oracle.weight_quant(w, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s, ws)
+    np.testing.assert_array_equal(c, wc)
+    dc, ds = oracle.weight_quant(w, lu, oracle.DENSE64)
+    wf = np.abs(inputs.bf16_bits_to_f32(w).astype(np.float64))
+    bound = np.concatenate([wf[:, 32 * j:32 * j + 32] @ np.abs(oracle.block_inverse_matrix(lu[j])).T
+                            for j in range(nb)], 1)
+    assert_codes_within_tie_tolerance(c, s, dc, ds, oracle.weight_transform(w, lu, oracle.DENSE64),
+                                      bound)
+
+
+# --------------------------------------------------------------------------
+# the W4A4 consumer
+# --------------------------------------------------------------------------
+def _gemm_reference(ac, as_, wc, ws):
+    A = oracle.mxfp4_dequant(ac, as_)
+    W = oracle.mxfp4_dequant(wc, ws)
+    Y = oracle.matmul_nt(A, W)
+    B = oracle.matmul_nt(np.abs(A), np.abs(W))
+    return Y, B
+
+
+def _assert_gemm_close(y_bits, Y, B, K):
+    """bf16 of an fp32-accumulated sum of exact products: within half a bf16
+    step of the fp64 sum plus K * 2^-23 of sum |a||w| (fp32 accumulation).
+    Half a bf16 step is up to 2^-8 of the value, so the same bound holds
+    normwise; in addition at least 90 % of the outputs must equal the bf16
+    rounding (nearest even) of the fp64 sum itself."""
+    y = inputs.bf16_bits_to_f32(y_bits).astype(np.float64)
+    err = np.abs(y - Y)
+    tol = 2.0 ** -8 * np.abs(Y) + K * 2.0 ** -23 * B + 1e-30
+    assert np.all(err <= tol), f"{int((err > tol).sum())} outputs off"
+    assert np.linalg.norm(y - Y) <= 2.0 ** -8 * np.linalg.norm(Y) + K * 2.0 ** -23 * np.linalg.norm(B)
+    exact = np.mean(np.asarray(y_bits, np.uint16) == inputs.f64_to_bf16_bits(Y))
+    assert exact >= 0.9, f"only {exact:.3f} of the outputs are the rounded fp64 sum"
+
+
+def _random_mxfp4(g, rows, k, lo=118, hi=128):
+    codes = g.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    scales = g.integers(lo, hi, (rows, k // 32), dtype=np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (128, 256, 256), (100, 300, 384),
+                                   (1, 17, 128), (257, 129, 512)])
+def test_gemm_random_mxfp4(torch_cuda, M, N, K):
+    torch = torch_cuda
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    Y, B = _gemm_reference(ac, as_, wc, ws)
+    _assert_gemm_close(yb, Y, B, K)
+
+
+def test_gemm_full_size_sampled_rows(torch_cuda):
+    """4608 x 12288 x 3072, the FLUX attention-projection consumer: quantizer
+    output times prepared weights; 24 sampled rows checked against the fp64
+    product of the dequantised operands."""
+    torch = torch_cuda
+    x = inputs.activation("flux_attn")
+    lu = inputs.lu_params("flux_attn")
+    w = inputs.gemm_weight()
+    xd, lud = to_gpu_bf16(x), to_gpu(lu)
+    ac, as_ = kq.transform_quant(xd, lud)
+    wc, ws = kq.weight_quant(to_gpu_bf16(w), lud)
+    y = kq.w4a4_gemm(ac, as_, wc, ws)
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    rows = np.sort(np.random.default_rng(9).choice(x.shape[0], 24, replace=False))
+    acn, asn, wcn, wsn = _np(ac), _np(as_), _np(wc), _np(ws)
+    Y, B = _gemm_reference(acn[rows], asn[rows], wcn, wsn)
+    _assert_gemm_close(yb[rows], Y, B, x.shape[1])
+    # end to end against the unquantised product X W^T on the sampled rows
+    xf = inputs.bf16_bits_to_f32(x[rows]).astype(np.float64)
+    wf = inputs.bf16_bits_to_f32(w).astype(np.float64)
+    ref = xf @ wf.T
+    got = inputs.bf16_bits_to_f32(yb[rows]).astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    _log(f"W4A4 end-to-end rel. error vs X W^T (KroQuant, random params): {rel:.4f}")
+    assert rel < 0.5

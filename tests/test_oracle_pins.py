@@ -453,3 +453,40 @@ def test_forward_error_scale_closed_form_at_hadamard_start(oracle):
     xf = np.abs(inputs.bf16_bits_to_f32(x).astype(np.float64)).reshape(x.shape[0], -1, 32)
     want = np.repeat(xf.sum(axis=2), 32, axis=1) / np.sqrt(32)
     np.testing.assert_allclose(b, want, rtol=1e-6)
+
+
+def test_weight_transform_preserves_the_product(oracle):
+    """LRQ-DiT Eq. (2) with an invertible T: (X T)(W T^-T)^T = X W^T, here
+    block by block along K with the fp64 definitions."""
+    g = np.random.default_rng(21)
+    nb = 3
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    x = inputs.f64_to_bf16_bits(g.standard_normal((5, nb * 32)))
+    w = inputs.f64_to_bf16_bits(g.standard_normal((7, nb * 32)))
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    wf = inputs.bf16_bits_to_f32(w).astype(np.float64)
+    xt = np.concatenate([xf[:, 32 * j:32 * j + 32] @ oracle.block_matrix(lu[j]) for j in range(nb)], 1)
+    wt = oracle.weight_transform(w, lu, oracle.DENSE64).astype(np.float64)
+    np.testing.assert_allclose(xt @ wt.T, xf @ wf.T, rtol=1e-5, atol=1e-5)
+    # and the weight transform is w times the transposed inverse block
+    for j in range(nb):
+        np.testing.assert_allclose(wt[:, 32 * j:32 * j + 32],
+                                   wf[:, 32 * j:32 * j + 32] @ np.linalg.inv(oracle.block_matrix(lu[j])).T,
+                                   rtol=1e-5, atol=1e-6)
+
+
+def test_weight_staged32_matches_dense64(oracle):
+    g = np.random.default_rng(22)
+    nb = 8
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.1, (nb, 5, 3))).astype(np.float32)
+    w = inputs.f64_to_bf16_bits(g.normal(0, 0.02, (64, nb * 32)))
+    y64 = oracle.weight_transform(w, lu, oracle.DENSE64).astype(np.float64)
+    y32 = oracle.weight_transform(w, lu, oracle.STAGED32).astype(np.float64)
+    wf = np.abs(inputs.bf16_bits_to_f32(w).astype(np.float64))
+    bound = np.concatenate([wf[:, 32 * j:32 * j + 32] @ np.abs(np.linalg.inv(oracle.block_matrix(lu[j]))).T
+                            for j in range(nb)], 1)
+    assert np.all(np.abs(y32 - y64) <= 1e-5 * bound + 1e-30)
+    # identity parameters leave the weights unchanged
+    ident = np.tile(np.array([0.0, 1.0, 0.0], np.float32), (nb, 5, 1))
+    np.testing.assert_array_equal(oracle.weight_transform(w, ident, oracle.STAGED32),
+                                  inputs.bf16_bits_to_f32(w))
