@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
 static int mfma_tiles_per_wave() {
     static int cached = 0;
     if (cached == 0) {
-        int v = 4;
+        int v = 2;
         const char *e = getenv("KQ_MFMA_TILES_PER_WAVE");
         if (e) {
             int q = atoi(e);

@@ -417,14 +417,16 @@ struct Plan {
     int tstep;  // tokens between consecutive units of a lane
 };
 
-// Units per lane: 4 by default (enough requests in flight per lane to cover
-// the memory latency, while the per-lane constant setup is amortised over
-// four blocks).  KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for
-// launch-geometry sweeps.
+// Units per lane: 1 by default.  More units per lane amortise the per-block
+// constant setup (fewer VALU instructions per unit), but on gfx950 the
+// launch is short enough that the number of resident waves decides: one
+// unit per lane (occupancy 7, every wave resident from the start) measured
+// 3-8 % faster than 2, 4 or 8 units per lane on 4608 x 3072.
+// KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
 static int units_per_lane() {
     static int cached = 0;
     if (cached == 0) {
-        int v = 4;
+        int v = 1;
         const char *e = getenv("KQ_UNITS_PER_LANE");
         if (e) {
             int p = atoi(e);
