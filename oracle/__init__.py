@@ -55,6 +55,12 @@ _SIGS = {
     "kqo_block_weight_staged32": (None, [_P, _P, _P]),
     "kqo_weight_transform": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _P, _INT]),
     "kqo_weight_quant": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _P, _P, _INT]),
+    "kqo_adaln_modulate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _INT,
+                                  _P, _P, _P, _INT]),
+    "kqo_adaln_transform_quant": (_INT, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float,
+                                         _P, _INT, _P, _P, _INT]),
+    "kqo_adaln_bound": (_INT, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
+                               _INT]),
 }
 
 _lib = None
@@ -333,3 +339,56 @@ def weight_quant(w_bits, lu, mode=STAGED32, k=None, threads=None):
                                 _ptr(scales), threads or default_threads())
     _check(rc, "kqo_weight_quant")
     return codes, scales
+
+
+# ---- AdaLN-modulated input ---------------------------------------------------
+def _adaln_args(x_bits, shift, scale, rows_per_sample, d):
+    x_bits, tokens, d, ld = _x_args(x_bits, d)
+    rps = tokens if rows_per_sample is None else int(rows_per_sample)
+    samples = max(1, -(-tokens // max(rps, 1)))
+    shift = np.ascontiguousarray(shift, np.float32).reshape(-1, d)
+    scale = np.ascontiguousarray(scale, np.float32).reshape(-1, d)
+    assert shift.shape[0] >= samples and scale.shape[0] >= samples, "one shift/scale row per sample"
+    return x_bits, tokens, d, ld, shift, scale, rps
+
+
+def adaln_modulate(x_bits, shift, scale, rows_per_sample=None, eps=1e-6, mode=STAGED32,
+                   d=None, threads=None):
+    """h = LN(x) * (1 + scale_s) + shift_s (fp32), with each row's mean and
+    1/sqrt(var + eps)."""
+    x_bits, tokens, d, ld, shift, scale, rps = _adaln_args(x_bits, shift, scale,
+                                                           rows_per_sample, d)
+    h = np.zeros((tokens, d), np.float32)
+    mean = np.zeros(tokens, np.float32)
+    rstd = np.zeros(tokens, np.float32)
+    rc = lib().kqo_adaln_modulate(_ptr(x_bits), tokens, d, ld, _ptr(shift), _ptr(scale), rps,
+                                  float(eps), mode, _ptr(h), _ptr(mean), _ptr(rstd),
+                                  threads or default_threads())
+    _check(rc, "kqo_adaln_modulate")
+    return h, mean, rstd
+
+
+def adaln_transform_quant(x_bits, shift, scale, lu, rows_per_sample=None, eps=1e-6,
+                          mode=STAGED32, d=None, threads=None):
+    x_bits, tokens, d, ld, shift, scale, rps = _adaln_args(x_bits, shift, scale,
+                                                           rows_per_sample, d)
+    lu = _lu_arg(lu, d)
+    codes = np.zeros((tokens, d // 2), np.uint8)
+    scales = np.zeros((tokens, d // 32), np.uint8)
+    rc = lib().kqo_adaln_transform_quant(_ptr(x_bits), tokens, d, ld, _ptr(shift), _ptr(scale),
+                                         rps, float(eps), _ptr(lu), mode, _ptr(codes),
+                                         _ptr(scales), threads or default_threads())
+    _check(rc, "kqo_adaln_transform_quant")
+    return codes, scales
+
+
+def adaln_bound(x_bits, shift, scale, lu, rows_per_sample=None, eps=1e-6, d=None,
+                threads=None) -> np.ndarray:
+    x_bits, tokens, d, ld, shift, scale, rps = _adaln_args(x_bits, shift, scale,
+                                                           rows_per_sample, d)
+    lu = _lu_arg(lu, d)
+    bound = np.zeros((tokens, d), np.float64)
+    rc = lib().kqo_adaln_bound(_ptr(x_bits), tokens, d, ld, _ptr(shift), _ptr(scale), rps,
+                               float(eps), _ptr(lu), _ptr(bound), threads or default_threads())
+    _check(rc, "kqo_adaln_bound")
+    return bound

@@ -726,3 +726,211 @@ int kqo_matmul_nt(const float *A, const float *W, int64_t M, int64_t N, int64_t 
     parallel_rows(row_matmul, &c, M, threads);
     return 0;
 }
+
+/* ======================================================================== */
+/* AdaLN-modulated input ([KQ-sum] "Problem": adaptive LayerNorm in the      */
+/* diffusion-transformer blocks is why the transform has to run online)      */
+/* ======================================================================== */
+/*
+ * h = LN(x) * (1 + scale_s) + shift_s per row, LN over the row's d channels
+ * with no affine part, population variance and eps inside the square root;
+ * row t uses the modulation vectors of sample s = t / rows_per_sample.
+ *
+ * DENSE64 is the definition: mean and variance (two passes) in fp64,
+ * n = (x - mean) / sqrt(var + eps), h = n * (1 + scale) + shift, all fp64.
+ *
+ * STAGED32 is the fixed fp32 order of the GPU kernel:
+ *   block partial  s_j = (((x_0 + x_1) + x_2) + ...) + x_31 of block j;
+ *   row total      64 lanes: lane l starts from s_l (0 when l >= nb), adds
+ *                  s_{l+64}, s_{l+128}, ... in turn; then six exchange
+ *                  steps: for m = 1, 2, 4, 8, 16, 32 every lane adds
+ *                  the value of lane l ^ m; the total is lane 0's value;
+ *   mean           = total / d;
+ *   c_k            = x_k - mean;
+ *   block partial  q_j = fma(c_31, c_31, ... fma(c_1, c_1, fma(c_0, c_0, 0)));
+ *   row total      as above, var = total / d;
+ *   rstd           = 1 / sqrt(var + eps) (each step correctly rounded);
+ *   h_k            = fma(c_k * rstd, 1 + scale_k, shift_k), 1 + scale_k in fp32.
+ */
+static float staged_row_total(const float *part, int64_t nb) {
+    float acc[64], nxt[64];
+    for (int l = 0; l < 64; ++l) {
+        float a = l < nb ? part[l] : 0.0f;
+        for (int64_t j = l + 64; j < nb; j += 64) a = a + part[j];
+        acc[l] = a;
+    }
+    for (int m = 1; m < 64; m <<= 1) {
+        for (int l = 0; l < 64; ++l) nxt[l] = acc[l] + acc[l ^ m];
+        memcpy(acc, nxt, sizeof acc);
+    }
+    return acc[0];
+}
+
+typedef struct {
+    const uint16_t *x;
+    int64_t d, ld, rps;
+    const float *shift, *scale, *lu;
+    float eps;
+    int mode;
+    float *h, *mean, *rstd;
+    uint8_t *codes, *scales;
+    double *bound;
+} ad_ctx;
+
+/* Row t: the modulated values, fp64 (DENSE64) or fp32 (STAGED32), plus the
+ * row statistics in the same mode. */
+static void adaln_row(const ad_ctx *c, int64_t t, double *h64, float *h32, double *mu_out,
+                      double *rstd_out) {
+    const uint16_t *xr = c->x + t * c->ld;
+    const int64_t d = c->d, nb = d / 32, s = t / c->rps;
+    const float *sh = c->shift + s * d, *sc = c->scale + s * d;
+    if (c->mode == KQO_DENSE64) {
+        double sum = 0.0, sq = 0.0;
+        for (int64_t k = 0; k < d; ++k) sum += (double)kqo_bf16_to_f32(xr[k]);
+        const double mu = sum / (double)d;
+        for (int64_t k = 0; k < d; ++k) {
+            const double cdev = (double)kqo_bf16_to_f32(xr[k]) - mu;
+            sq += cdev * cdev;
+        }
+        const double rstd = 1.0 / sqrt(sq / (double)d + (double)c->eps);
+        for (int64_t k = 0; k < d; ++k) {
+            const double n = ((double)kqo_bf16_to_f32(xr[k]) - mu) * rstd;
+            h64[k] = n * (1.0 + (double)sc[k]) + (double)sh[k];
+        }
+        if (mu_out) *mu_out = mu;
+        if (rstd_out) *rstd_out = rstd;
+        return;
+    }
+    float *part = (float *)calloc((size_t)nb, sizeof(float));
+    for (int64_t j = 0; j < nb; ++j) {
+        float a = kqo_bf16_to_f32(xr[j * 32]);
+        for (int k = 1; k < 32; ++k) a = a + kqo_bf16_to_f32(xr[j * 32 + k]);
+        part[j] = a;
+    }
+    const float mean = staged_row_total(part, nb) / (float)d;
+    for (int64_t j = 0; j < nb; ++j) {
+        float q = 0.0f;
+        for (int k = 0; k < 32; ++k) {
+            const float cdev = kqo_bf16_to_f32(xr[j * 32 + k]) - mean;
+            q = fmaf(cdev, cdev, q);
+        }
+        part[j] = q;
+    }
+    const float var = staged_row_total(part, nb) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + c->eps);
+    free(part);
+    for (int64_t k = 0; k < d; ++k) {
+        const float cdev = kqo_bf16_to_f32(xr[k]) - mean;
+        h32[k] = fmaf(cdev * rstd, 1.0f + sc[k], sh[k]);
+    }
+    if (mu_out) *mu_out = mean;
+    if (rstd_out) *rstd_out = rstd;
+}
+
+static void row_adaln_modulate(void *vc, int64_t t) {
+    ad_ctx *c = (ad_ctx *)vc;
+    double *h64 = (double *)malloc((size_t)c->d * sizeof(double));
+    double mu, rstd;
+    adaln_row(c, t, h64, c->h + t * c->d, &mu, &rstd);
+    if (c->mode == KQO_DENSE64)
+        for (int64_t k = 0; k < c->d; ++k) c->h[t * c->d + k] = (float)h64[k];
+    if (c->mean) c->mean[t] = (float)mu;
+    if (c->rstd) c->rstd[t] = (float)rstd;
+    free(h64);
+}
+
+static void row_adaln_quant(void *vc, int64_t t) {
+    ad_ctx *c = (ad_ctx *)vc;
+    const int64_t d = c->d, nb = d / 32;
+    double *h64 = (double *)malloc((size_t)d * sizeof(double));
+    float *h32 = (float *)malloc((size_t)d * sizeof(float));
+    adaln_row(c, t, h64, h32, NULL, NULL);
+    for (int64_t j = 0; j < nb; ++j) {
+        const float *p = c->lu + j * 15;
+        float yb[32];
+        if (c->mode == KQO_DENSE64) {
+            double T[1024];
+            kqo_block_matrix(p, T);
+            for (int k = 0; k < 32; ++k) {
+                double acc = 0.0;
+                for (int i = 0; i < 32; ++i) acc += h64[j * 32 + i] * T[i * 32 + k];
+                yb[k] = (float)acc;
+            }
+        } else {
+            kqo_block_transform_staged32(h32 + j * 32, p, yb);
+        }
+        kqo_mxfp4_block(yb, c->codes + t * (d / 2) + j * 16, c->scales + t * nb + j);
+    }
+    free(h64);
+    free(h32);
+}
+
+/* Forward-error scale of the STAGED32 values against DENSE64, per output:
+ * sum_i (|1 + scale_i| (|n_i| + mean_j |x_j| * rstd) + |h_i|) |T_ik| (fp64). */
+static void row_adaln_bound(void *vc, int64_t t) {
+    ad_ctx *c = (ad_ctx *)vc;
+    const int64_t d = c->d, nb = d / 32, s = t / c->rps;
+    const uint16_t *xr = c->x + t * c->ld;
+    const float *sc = c->scale + s * d;
+    double *h64 = (double *)malloc((size_t)d * sizeof(double));
+    double mu, rstd, amean = 0.0;
+    ad_ctx cd = *c;
+    cd.mode = KQO_DENSE64;
+    adaln_row(&cd, t, h64, NULL, &mu, &rstd);
+    for (int64_t k = 0; k < d; ++k) amean += fabs((double)kqo_bf16_to_f32(xr[k]));
+    amean /= (double)d;
+    for (int64_t j = 0; j < nb; ++j) {
+        double T[1024], e[32];
+        kqo_block_matrix(c->lu + j * 15, T);
+        for (int i = 0; i < 32; ++i) {
+            const int64_t k = j * 32 + i;
+            const double n = ((double)kqo_bf16_to_f32(xr[k]) - mu) * rstd;
+            e[i] = fabs(1.0 + (double)sc[k]) * (fabs(n) + amean * rstd) + fabs(h64[k]);
+        }
+        for (int k = 0; k < 32; ++k) {
+            double acc = 0.0;
+            for (int i = 0; i < 32; ++i) acc += e[i] * fabs(T[i * 32 + k]);
+            c->bound[t * d + j * 32 + k] = acc;
+        }
+    }
+    free(h64);
+}
+
+static int bad_adaln(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                     const float *shift, const float *scale, int64_t rps, float eps) {
+    return !x || !shift || !scale || bad_shape(tokens, d, ld) || rps < 1 || !(eps >= 0.0f);
+}
+
+int kqo_adaln_modulate(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                       const float *shift, const float *scale, int64_t rows_per_sample,
+                       float eps, int mode, float *h, float *mean, float *rstd, int threads) {
+    if (bad_adaln(x, tokens, d, ld, shift, scale, rows_per_sample, eps) || !h) return -1;
+    ad_ctx c = {x, d, ld, rows_per_sample, shift, scale, NULL, eps, mode, h, mean, rstd,
+                NULL, NULL, NULL};
+    parallel_rows(row_adaln_modulate, &c, tokens, threads);
+    return 0;
+}
+
+int kqo_adaln_transform_quant(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                              const float *shift, const float *scale, int64_t rows_per_sample,
+                              float eps, const float *lu, int mode, uint8_t *codes,
+                              uint8_t *scales, int threads) {
+    if (bad_adaln(x, tokens, d, ld, shift, scale, rows_per_sample, eps) || !lu || !codes ||
+        !scales)
+        return -1;
+    ad_ctx c = {x, d, ld, rows_per_sample, shift, scale, lu, eps, mode, NULL, NULL, NULL,
+                codes, scales, NULL};
+    parallel_rows(row_adaln_quant, &c, tokens, threads);
+    return 0;
+}
+
+int kqo_adaln_bound(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                    const float *shift, const float *scale, int64_t rows_per_sample, float eps,
+                    const float *lu, double *bound, int threads) {
+    if (bad_adaln(x, tokens, d, ld, shift, scale, rows_per_sample, eps) || !lu || !bound)
+        return -1;
+    ad_ctx c = {x, d, ld, rows_per_sample, shift, scale, lu, eps, KQO_DENSE64, NULL, NULL,
+                NULL, NULL, NULL, bound};
+    parallel_rows(row_adaln_bound, &c, tokens, threads);
+    return 0;
+}

@@ -141,6 +141,30 @@ int kqo_weight_transform(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
 int kqo_weight_quant(const uint16_t *w, int64_t rows, int64_t k, int64_t ld,
                      const float *lu, int mode, uint8_t *codes, uint8_t *scales, int threads);
 
+/* AdaLN-modulated quantizer input ([KQ-sum] "Problem": adaptive LayerNorm
+ * in the transformer blocks is why the transform runs online):
+ * h = LN(x) * (1 + scale_s) + shift_s, LN over the d channels of a row (no
+ * affine part, population variance, eps inside the square root), s = t /
+ * rows_per_sample; shift and scale are fp32 [samples][d].  DENSE64 is fp64
+ * throughout; STAGED32 follows the fixed fp32 order of the GPU kernel (see
+ * the comment at adaln_row() in kq_oracle.c).  kqo_adaln_modulate writes h
+ * (fp32; DENSE64 rounds the fp64 value once) and, when the pointers are not
+ * NULL, each row's mean and 1/sqrt(var + eps).  kqo_adaln_transform_quant
+ * quantizes h * T to MXFP4 (DENSE64: fp64 h and fp64 product, rounded once to
+ * fp32 before the MXFP4 decisions).  kqo_adaln_bound is the forward-error
+ * scale of STAGED32 against DENSE64 per output element:
+ * sum_i (|1 + scale_i| (|n_i| + mean|x| * rstd) + |h_i|) |T_ik|. */
+int kqo_adaln_modulate(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                       const float *shift, const float *scale, int64_t rows_per_sample,
+                       float eps, int mode, float *h, float *mean, float *rstd, int threads);
+int kqo_adaln_transform_quant(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                              const float *shift, const float *scale, int64_t rows_per_sample,
+                              float eps, const float *lu, int mode, uint8_t *codes,
+                              uint8_t *scales, int threads);
+int kqo_adaln_bound(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                    const float *shift, const float *scale, int64_t rows_per_sample, float eps,
+                    const float *lu, double *bound, int threads);
+
 /* Y[m][n] = sum_k A[m][k] * W[n][k] in fp64 (A, W fp32 row-major). */
 int kqo_matmul_nt(const float *A, const float *W, int64_t M, int64_t N, int64_t K,
                   double *Y, int threads);

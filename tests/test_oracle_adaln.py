@@ -1,0 +1,138 @@
+"""Pins of the oracle's AdaLN-modulated quantizer input against what the
+mathematics fixes: closed-form moments, the invariance of LayerNorm under
+x -> a*x + b, the modulation identities, sample indexing and exact integer
+sums (every block counted once by the fixed-order reduction)."""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp4_activation_quantizer_amd import inputs
+from parity import assert_codes_within_tie_tolerance
+
+
+def _bits(a):
+    return inputs.f64_to_bf16_bits(np.asarray(a, np.float64))
+
+
+def test_adaln_closed_form_moments():
+    # x_k = (k mod 16) - 8: mean -1/2, population variance 21.25, all exact in
+    # bf16 and in the fp32 partial sums.
+    d = 256
+    x = _bits(np.tile(np.arange(d) % 16 - 8.0, (3, 1)))
+    z = np.zeros(d, np.float32)
+    eps = 1e-6
+    rstd_exact = 1.0 / np.sqrt(21.25 + eps)
+    want = (np.arange(d) % 16 - 7.5) * rstd_exact
+    for mode in (oracle.DENSE64, oracle.STAGED32):
+        h, mean, rstd = oracle.adaln_modulate(x, z, z, eps=eps, mode=mode)
+        assert np.all(mean == -0.5)
+        assert np.allclose(rstd, rstd_exact, rtol=2e-7, atol=0)
+        assert np.allclose(h, want[None, :], rtol=4e-7, atol=0)
+    # the fixed fp32 order: every partial sum is exact, so the statistics are
+    # the correctly rounded fp32 operations on exact values
+    h, mean, rstd = oracle.adaln_modulate(x, z, z, eps=eps, mode=oracle.STAGED32)
+    r32 = np.float32(1.0) / np.sqrt(np.float32(21.25) + np.float32(eps), dtype=np.float32)
+    assert np.all(rstd == r32)
+
+
+def test_layernorm_invariant_under_affine_maps_of_x():
+    g = np.random.default_rng(1)
+    xi = g.integers(-20, 21, size=(5, 384)).astype(np.float64)
+    sh = g.normal(size=384).astype(np.float32)
+    sc = g.normal(scale=0.3, size=384).astype(np.float32)
+    h1, _, _ = oracle.adaln_modulate(_bits(xi), sh, sc, eps=0.0, mode=oracle.DENSE64)
+    h2, _, _ = oracle.adaln_modulate(_bits(2 * xi + 4), sh, sc, eps=0.0, mode=oracle.DENSE64)
+    h3, _, _ = oracle.adaln_modulate(_bits(-xi), sh, sc, eps=0.0, mode=oracle.DENSE64)
+    assert np.allclose(h1, h2, rtol=1e-6, atol=1e-6)
+    n1 = (h1 - sh) / (1 + sc)  # the normalised row
+    n3 = (h3 - sh) / (1 + sc)
+    assert np.allclose(n1, -n3, rtol=1e-5, atol=1e-5)
+    assert np.allclose(n1.mean(1), 0, atol=1e-5)
+    assert np.allclose((n1.astype(np.float64) ** 2).mean(1), 1, atol=1e-5)
+
+
+@pytest.mark.parametrize("mode", [oracle.DENSE64, oracle.STAGED32])
+def test_modulation_identities(mode):
+    g = np.random.default_rng(2)
+    x = _bits(g.normal(size=(4, 128)))
+    sh = g.normal(size=128).astype(np.float32)
+    # scale = -1 removes the normalised part: h = shift exactly
+    h, _, _ = oracle.adaln_modulate(x, sh, -np.ones(128, np.float32), mode=mode)
+    assert np.array_equal(h, np.broadcast_to(sh, h.shape))
+    # a shift adds itself (up to the final rounding)
+    z = np.zeros(128, np.float32)
+    h0, _, _ = oracle.adaln_modulate(x, z, z, mode=mode)
+    hb, _, _ = oracle.adaln_modulate(x, sh, z, mode=mode)
+    assert np.allclose(hb - h0, sh, rtol=0, atol=2e-6 * (np.abs(h0) + np.abs(sh)).max())
+
+
+def test_rows_use_their_own_sample():
+    g = np.random.default_rng(3)
+    x = _bits(g.normal(size=(7, 64)))
+    shift = np.arange(1, 3, dtype=np.float32)[:, None] * np.ones((2, 64), np.float32)
+    scale = -np.ones((2, 64), np.float32)
+    for mode in (oracle.DENSE64, oracle.STAGED32):
+        h, _, _ = oracle.adaln_modulate(x, shift, scale, rows_per_sample=4, mode=mode)
+        assert np.all(h[:4] == 1.0) and np.all(h[4:] == 2.0)
+
+
+@pytest.mark.parametrize("d", [32, 1152, 3072, 12288])
+def test_staged_reduction_counts_every_block_once(d):
+    # integer data: every fp32 partial and total is exact whatever the order,
+    # so the staged mean is the correctly rounded total / d
+    g = np.random.default_rng(d)
+    xi = g.integers(-8, 9, size=(6, d)).astype(np.float64)
+    z = np.zeros(d, np.float32)
+    _, mean, _ = oracle.adaln_modulate(_bits(xi), z, z, mode=oracle.STAGED32)
+    total = xi.sum(1)
+    want = (total.astype(np.float32) / np.float32(d)).astype(np.float32)
+    assert np.array_equal(mean, want)
+
+
+def test_constant_and_nonfinite_rows():
+    d = 64
+    x = np.full((3, d), 1.5)
+    x[1] = np.linspace(-1, 1, d)
+    x[2, 5] = np.nan
+    sh = np.linspace(0.1, 0.7, d).astype(np.float32)
+    z = np.zeros(d, np.float32)
+    lu = inputs.hadamard_init(d // 32)
+    for mode in (oracle.DENSE64, oracle.STAGED32):
+        h, _, rstd = oracle.adaln_modulate(_bits(x), sh, z, eps=1e-6, mode=mode)
+        assert np.array_equal(h[0], sh)                    # zero variance: h = shift
+        assert np.isclose(rstd[0], 1e3, rtol=1e-6)         # 1/sqrt(eps)
+        assert np.all(np.isnan(h[2]))
+        codes, scales = oracle.adaln_transform_quant(_bits(x), sh, z, lu, mode=mode)
+        assert np.all(scales[2] == 0xFF) and np.all(codes[2] == 0)
+        assert np.all(scales[:2] != 0xFF)
+
+
+def test_identity_params_reduce_to_plain_mxfp4_of_h():
+    g = np.random.default_rng(4)
+    d = 256
+    x = _bits(g.normal(size=(8, d)) * np.where(g.random(d) < 0.05, 50, 1))
+    sh = g.normal(scale=0.2, size=d).astype(np.float32)
+    sc = g.normal(scale=0.2, size=d).astype(np.float32)
+    ident = np.tile(np.array([0.0, 1.0, 0.0], np.float32), (d // 32) * 5)
+    h, _, _ = oracle.adaln_modulate(x, sh, sc, mode=oracle.STAGED32)
+    c1, s1 = oracle.adaln_transform_quant(x, sh, sc, ident, mode=oracle.STAGED32)
+    c2, s2 = oracle.mxfp4_quant(h)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_staged_matches_definition_within_the_forward_error_bound():
+    g = np.random.default_rng(5)
+    tokens, d = 96, 3072
+    x = inputs.activation("flux_attn")[:tokens]
+    lu = inputs.lu_params("flux_attn")
+    sh = g.normal(scale=0.3, size=(2, d)).astype(np.float32)
+    sc = g.normal(scale=0.3, size=(2, d)).astype(np.float32)
+    cs, ss = oracle.adaln_transform_quant(x, sh, sc, lu, rows_per_sample=48, mode=oracle.STAGED32)
+    cd, sd = oracle.adaln_transform_quant(x, sh, sc, lu, rows_per_sample=48, mode=oracle.DENSE64)
+    # the definition's transformed values: fp64 h times fp64 T, rounded once
+    hd, _, _ = oracle.adaln_modulate(x, sh, sc, rows_per_sample=48, mode=oracle.DENSE64)
+    yd = np.concatenate([hd[:, 32 * j:32 * j + 32].astype(np.float64) @ oracle.block_matrix(lu[j])
+                         for j in range(d // 32)], 1)
+    bound = oracle.adaln_bound(x, sh, sc, lu, rows_per_sample=48)
+    nsc, ncode = assert_codes_within_tie_tolerance(cs, ss, cd, sd, yd, bound)
+    assert nsc <= 2
