@@ -21,6 +21,7 @@ timing, untimed launches run for 0.3 s so that the clocks have settled.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -72,6 +73,8 @@ KERNEL_MATCH = {
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
     "kq_w4a4_gemm": "w4a4_gemm_kernel",
+    "kq_adaln_transform_quant": "adaln_kernelILi2ELb1E",
+    "kq_adaln_modulate": "adaln_kernelILi2ELb0E",
 }
 
 PROFILE_COMMANDS = """\
@@ -189,7 +192,8 @@ def main() -> int:
     ap.add_argument("--kernel", default="kq_transform_quant",
                     choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
                              "kq_fwht32_quant", "kq_copy_ceiling", "kq_dequant_inverse",
-                             "kq_weight_quant", "kq_w4a4_gemm"],
+                             "kq_weight_quant", "kq_w4a4_gemm", "kq_adaln_transform_quant",
+                             "kq_adaln_unfused"],
                     help="the entry point --kernel-only times")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise rocprofv3 CSV outputs under DIR into profiles/ and exit")
@@ -271,8 +275,26 @@ def main() -> int:
         gemm.update(n=wn, k=wk, flops=2.0 * T * wn * wk,
                     weight_bytes=wn * wk * (2 + 0.5 + 1 / 32))
 
+    # AdaLN-fused quantizer: the same rotating inputs read as the pre-norm
+    # stream, one sample's shift/scale; the unfused pipeline writes bf16 h.
+    shift_np, scale_np = inputs.modulation(args.workload, 1, d)
+    shift_d, scale_d = torch.from_numpy(shift_np).to(dev), torch.from_numpy(scale_np).to(dev)
+    need_h = (args.kernel_only and args.kernel == "kq_adaln_unfused") or \
+        not (args.kernel_only or args.no_peers)
+    hs = [torch.empty((T, d), dtype=torch.bfloat16, device=dev) for _ in range(R)] if need_h else []
+
     def argsets(fn_name):
         out = []
+        if fn_name == "kq_adaln_transform_quant":
+            return [(xs[i].data_ptr(), T, d, d, shift_d.data_ptr(), scale_d.data_ptr(), T,
+                     ctypes.c_float(1e-6), lu_d.data_ptr(), codes[i].data_ptr(),
+                     scales[i].data_ptr(), sp) for i in range(R)]
+        if fn_name == "kq_adaln_modulate":
+            return [(xs[i].data_ptr(), T, d, d, shift_d.data_ptr(), scale_d.data_ptr(), T,
+                     ctypes.c_float(1e-6), hs[i].data_ptr(), d, sp) for i in range(R)]
+        if fn_name == "kq_transform_quant_from_h":
+            return [(hs[i].data_ptr(), T, d, d, lu_d.data_ptr(), codes[i].data_ptr(),
+                     scales[i].data_ptr(), sp) for i in range(R)]
         if fn_name == "kq_w4a4_gemm":
             for i in range(R):  # A: the quantized activations of set i
                 y = gemm["y"][i % 2]
@@ -296,9 +318,17 @@ def main() -> int:
                 out.append((xp, T, d, d, cp, scp, sp))
         return out
 
+    def unfused(*a):
+        st = L.kq_adaln_modulate(*a[0])
+        return st if st != 0 else L.kq_transform_quant(*a[1])
+
     def timed(fn_name, steps, warmup):
-        fn = getattr(L, fn_name)
-        a = argsets(fn_name)
+        if fn_name == "kq_adaln_unfused":  # two launches per step
+            fn = unfused
+            a = list(zip(argsets("kq_adaln_modulate"), argsets("kq_transform_quant_from_h")))
+        else:
+            fn = getattr(L, fn_name)
+            a = argsets(fn_name)
         n_a = len(a)
         for i in range(warmup):
             st = fn(*a[i % n_a])
@@ -333,6 +363,8 @@ def main() -> int:
         rec = {"kernel": args.kernel, "ms_per_step": ms}
         if args.kernel == "kq_w4a4_gemm":
             rec["TFLOPs"] = gemm["flops"] / (ms * 1e-3) / 1e12
+        elif args.kernel in ("kq_adaln_transform_quant", "kq_adaln_unfused"):
+            rec["GBps_fused_bytes"] = nbytes / (ms * 1e-3) / 1e9
         elif args.kernel == "kq_weight_quant":
             rec["GBps"] = gemm["weight_bytes"] / (ms * 1e-3) / 1e9
         else:
@@ -353,6 +385,15 @@ def main() -> int:
             extra[name] = {"ms_per_step": round(pms, 6),
                            "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+        # AdaLN + quantizer: fused (one pass, same bytes as the quantizer) vs
+        # modulate-to-bf16 then quantize (4 more bytes per element through HBM)
+        fms = timed("kq_adaln_transform_quant", args.steps, args.warmup)
+        ums = timed("kq_adaln_unfused", args.steps, args.warmup)
+        extra["adaln_fused"] = {"ms_per_step": round(fms, 6),
+                                "GBps": round(nbytes / (fms * 1e-3) / 1e9, 1)}
+        extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
+                                  "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
+                                  "fused_speedup": round(ums / fms, 3)}
     if gemm:
         timed("kq_transform_quant", R, 0)  # A operands: fresh quantizer outputs
         pms = timed("kq_weight_quant", max(10, args.steps // 10), max(2, args.warmup // 10))

@@ -202,6 +202,48 @@ kq_status kq_w4a4_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
                        int64_t K, void *y, int64_t ld_y, void *stream);
 
 /*
+ * kq_adaln_transform_quant — the quantizer fused with the adaptive LayerNorm
+ * that produces its input in a diffusion-transformer block (KroQuant summary,
+ * "Problem": AdaLN blocks are why the transform runs online).  One pass:
+ *   h = LN(x) * (1 + scale_s) + shift_s,  then y = h * T_j and MXFP4(y),
+ * LN over the d channels of each row with no affine part, population
+ * variance and eps inside the square root; row t belongs to sample
+ * s = t / rows_per_sample.  The modulated tensor is never stored.
+ *
+ *   x        bf16 [tokens][ld_x], 16-byte aligned, ld_x % 8 == 0
+ *   shift    fp32 [ceil(tokens / rows_per_sample)][d], 16-byte aligned
+ *   scale    fp32, same shape (the modulation multiplies by 1 + scale)
+ *   rows_per_sample >= 1; eps >= 0 and finite
+ *   lu, codes, scales as for kq_transform_quant
+ *
+ * d % 32 == 0 and d <= 8192 (one sample's modulation vectors are staged in
+ * LDS); anything else returns KQ_ERR_SHAPE.
+ * Fixed fp32 order (results reproducible bit for bit): per 32-value block a
+ * sequential sum; per row, 64 lanes where lane l starts from block l's sum
+ * (0 when l >= d/32) and adds blocks l + 64, l + 128, ... in turn, then for
+ * m = 1, 2, 4, 8, 16, 32 every lane adds lane l ^ m's value; mean = total / d;
+ * c = x - mean; per block q = fma(c, c, q) from q = 0 over the 32 values in
+ * order, row total as before, var = total / d; rstd = 1 / sqrt(var + eps);
+ * h = fma(c * rstd, 1 + scale, shift); then the transform in the order of
+ * kq_transform_quant.
+ */
+kq_status kq_adaln_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                                   const float *shift, const float *scale,
+                                   int64_t rows_per_sample, float eps, const float *lu,
+                                   uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * kq_adaln_modulate — the same modulation alone, h rounded to bf16 (nearest
+ * even): the first kernel of the unfused pipeline (modulate, then
+ * kq_transform_quant), kept for comparison and for callers that need h.
+ *   h   bf16 [tokens][ld_h], 16-byte aligned, ld_h % 8 == 0, ld_h >= d (written)
+ * Other arguments and the operation order as for kq_adaln_transform_quant.
+ */
+kq_status kq_adaln_modulate(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                            const float *shift, const float *scale, int64_t rows_per_sample,
+                            float eps, void *h, int64_t ld_h, void *stream);
+
+/*
  * kq_copy_ceiling — not a quantizer: moves the same bytes as
  * kq_transform_quant (reads the bf16 tensor, writes d/2 + d/32 bytes per row)
  * with almost no arithmetic, to measure the achievable bandwidth of this

@@ -159,6 +159,32 @@ def smooth_multipliers(x_bits: np.ndarray, alpha: float = 0.5, floor: float = 1e
     return (np.maximum(a, floor) ** (-alpha)).astype(np.float32)
 
 
+def residual(name: str, tokens: int | None = None, d: int | None = None) -> np.ndarray:
+    """Pre-norm residual-stream rows for the AdaLN-fused quantizer, bf16 bits
+    [tokens][d]: N(0,1) scaled per token by lognormal(0, 0.5) and shifted per
+    token by N(0, 0.5), with 0.5 % of the channels x100 (the few very large
+    channels of a transformer's residual stream).  Defaults to the workload's
+    shape."""
+    w = WORKLOADS[name]
+    T = w.tokens if tokens is None else tokens
+    d = w.d if d is None else d
+    g = rng(w.wid, 2)
+    x = g.standard_normal((T, d)) * g.lognormal(0.0, 0.5, size=(T, 1)) + g.normal(0.0, 0.5, (T, 1))
+    x[:, _outlier_channels(g, d, 0.005)] *= 100.0
+    return f64_to_bf16_bits(x)
+
+
+def modulation(name: str, samples: int = 1, d: int | None = None):
+    """AdaLN shift and scale vectors (the per-sample outputs of the
+    conditioning projection), float32 [samples][d] each, N(0, 0.3)."""
+    w = WORKLOADS[name]
+    d = w.d if d is None else d
+    g = rng(w.wid, 3)
+    shift = g.normal(0.0, 0.3, (samples, d)).astype(np.float32)
+    scale = g.normal(0.0, 0.3, (samples, d)).astype(np.float32)
+    return shift, scale
+
+
 def gemm_weight() -> np.ndarray:
     """W4A4 consumer weights W [N=12288][K=3072] ~ N(0, 0.02), bf16 bits."""
     g = rng(GEMM_WID, 0)

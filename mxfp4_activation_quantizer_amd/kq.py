@@ -40,6 +40,10 @@ SIGNATURES = {
     "kq_weight_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_dequant_inverse": (_ST, [_P, _P, _I64, _I64, _P, _P, _I64, _P]),
     "kq_w4a4_gemm": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "kq_adaln_transform_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P,
+                                       _P, _P, _P]),
+    "kq_adaln_modulate": (_ST, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64,
+                                _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -120,6 +124,18 @@ def kq_dequant_inverse(codes, scales, tokens, d, lu, x_out, ld_out, stream=None)
 
 def kq_w4a4_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, ld_y, stream=None) -> int:
     return lib().kq_w4a4_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, ld_y, stream)
+
+
+def kq_adaln_transform_quant(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps, lu, codes,
+                             scales, stream=None) -> int:
+    return lib().kq_adaln_transform_quant(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps,
+                                          lu, codes, scales, stream)
+
+
+def kq_adaln_modulate(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps, h, ld_h,
+                      stream=None) -> int:
+    return lib().kq_adaln_modulate(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps, h, ld_h,
+                                   stream)
 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
@@ -266,3 +282,36 @@ def w4a4_gemm(a_codes, a_scales, w_codes, w_scales, y=None):
         a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
         M, N, K, y.data_ptr(), y.stride(0), _stream(a_codes)))
     return y
+
+
+def _rps(tokens: int, rows_per_sample) -> int:
+    return max(tokens, 1) if rows_per_sample is None else int(rows_per_sample)
+
+
+def adaln_transform_quant(x, shift, scale, lu, rows_per_sample=None, eps: float = 1e-6,
+                          d: int | None = None, codes=None, scales=None):
+    """MXFP4 of (LN(x) * (1 + scale_s) + shift_s) * T per 32-channel block, one
+    pass; shift/scale fp32 [samples][d] on the GPU, row t in sample
+    t // rows_per_sample (default: one sample)."""
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _check("kq_adaln_transform_quant", kq_adaln_transform_quant(
+        x.data_ptr(), tokens, d, ld, shift.data_ptr(), scale.data_ptr(),
+        _rps(tokens, rows_per_sample), float(eps), lu.data_ptr(), codes.data_ptr(),
+        scales.data_ptr(), _stream(x)))
+    return codes, scales
+
+
+def adaln_modulate(x, shift, scale, rows_per_sample=None, eps: float = 1e-6,
+                   d: int | None = None, h=None):
+    """bf16 LN(x) * (1 + scale_s) + shift_s."""
+    torch = _torch()
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    if h is None:
+        h = torch.empty((tokens, (d + 7) // 8 * 8), dtype=torch.bfloat16, device=x.device)[:, :d]
+    _check("kq_adaln_modulate", kq_adaln_modulate(
+        x.data_ptr(), tokens, d, ld, shift.data_ptr(), scale.data_ptr(),
+        _rps(tokens, rows_per_sample), float(eps), h.data_ptr(), h.stride(0), _stream(x)))
+    return h

@@ -105,6 +105,37 @@ def test_parameter_pointer_checks():
     assert g(A16, A16, A16, A16, 8, 16, 128, A16 + 2, 16) == kq.KQ_ERR_ALIGN
 
 
+def test_adaln_argument_checks():
+    q = kq.kq_adaln_transform_quant
+    m = kq.kq_adaln_modulate
+    ok = (A16, 4, 64, 64, A16, A16, 4, 1e-6)
+    assert q(None, 0, 64, 64, None, None, 1, 1e-6, None, None, None) == kq.KQ_OK
+    assert m(None, 0, 64, 64, None, None, 1, 1e-6, None, 64) == kq.KQ_OK
+    assert q(A16, 4, 48, 64, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_SHAPE    # d % 32
+    assert q(A16, 4, 8224, 8224, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_SHAPE  # d > 8192
+    assert q(A16, 4, 64, 32, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_SHAPE    # ld < d
+    assert q(A16, 4, 64, 64, A16, A16, 0, 1e-6, A16, A16, A16) == kq.KQ_ERR_SHAPE    # rows/sample
+    assert q(A16, 4, 64, 64, A16, A16, 4, -1.0, A16, A16, A16) == kq.KQ_ERR_SHAPE    # eps < 0
+    assert q(A16, 4, 64, 64, A16, A16, 4, float("nan"), A16, A16, A16) == kq.KQ_ERR_SHAPE
+    assert q(A16, 4, 64, 64, A16, A16, 4, float("inf"), A16, A16, A16) == kq.KQ_ERR_SHAPE
+    assert q(None, 4, 64, 64, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_NULL
+    assert q(A16, 4, 64, 64, None, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_NULL
+    assert q(A16, 4, 64, 64, A16, None, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_NULL
+    assert q(*ok, None, A16, A16) == kq.KQ_ERR_NULL
+    assert q(*ok, A16, None, A16) == kq.KQ_ERR_NULL
+    assert q(*ok, A16, A16, None) == kq.KQ_ERR_NULL
+    assert q(ODD, 4, 64, 64, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_ALIGN
+    assert q(A16, 4, 64, 68, A16, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_ALIGN
+    assert q(A16, 4, 64, 64, A16 + 4, A16, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_ALIGN
+    assert q(A16, 4, 64, 64, A16, A16 + 8, 4, 1e-6, A16, A16, A16) == kq.KQ_ERR_ALIGN
+    assert q(*ok, ODD, A16, A16) == kq.KQ_ERR_ALIGN
+    assert q(*ok, A16, A16 + 8, A16) == kq.KQ_ERR_ALIGN
+    assert m(*ok, None, 64) == kq.KQ_ERR_NULL
+    assert m(*ok, A16, 32) == kq.KQ_ERR_SHAPE
+    assert m(*ok, A16 + 2, 64) == kq.KQ_ERR_ALIGN
+    assert m(*ok, A16, 68) == kq.KQ_ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
