@@ -73,8 +73,8 @@ KERNEL_MATCH = {
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
     "kq_w4a4_gemm": "w4a4_gemm_kernel",
-    "kq_adaln_transform_quant": "adaln_kernelILi2ELb1E",
-    "kq_adaln_modulate": "adaln_kernelILi2ELb0E",
+    "kq_adaln_transform_quant": "adaln_kernelILi1ELb1E",
+    "kq_adaln_modulate": "adaln_kernelILi1ELb0E",
 }
 
 PROFILE_COMMANDS = """\

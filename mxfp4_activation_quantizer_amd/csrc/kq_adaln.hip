@@ -10,14 +10,16 @@
 //
 // Work decomposition.  A workgroup owns ROWS = G * U whole rows of one
 // sample: thread i handles block j = i mod nb of rows U*(i / nb) ..
-// U*(i / nb) + U - 1, so its Kronecker constants are set up once for U units.
+// U*(i / nb) + U - 1 (U = 1 by default).
 // The sample's modulation vectors (1 + scale and shift, fp32) are staged in
 // LDS.  The row statistics use a fixed order, so the result is reproducible
 // bit for bit:
 //   block partial   sequential sum over the block's 32 values;
 //   row total       wave-wide: lane l starts from partial l (0 past nb) and
 //                   adds partials l + 64, l + 128, ...; then for m = 1, 2, 4,
-//                   8, 16, 32 each lane adds lane l ^ m's value;
+//                   8, 16, 32 each lane adds lane l ^ m's value (DPP moves
+//                   and lane reads; every wave reduces the rows it needs, so
+//                   a launch has two workgroup barriers);
 //   mean = total / d; c = x - mean;
 //   block partial   fma(c_31, c_31, ... fma(c_0, c_0, 0));
 //   var = total / d; rstd = 1 / sqrt(var + eps) (correctly rounded steps);
@@ -52,26 +54,53 @@ struct AdalnArgs {
     int d, nb, G, wps;           // row groups per workgroup, workgroups per sample
 };
 
-// Sum over the 64 lanes of a wave of one value per lane, in the fixed
-// exchange order m = 1, 2, 4, ..., 32; every lane ends with the total.
-__device__ __forceinline__ float wave_total(float a) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) a = a + __shfl_xor(a, m, 64);
-    return a;
+// Sum over the 64 lanes of a wave in the exchange order m = 1, 2, 4, 8, 16,
+// 32 (each lane adds lane l ^ m's value).  Steps 1 and 2 are quad
+// permutations; after them the four lanes of a quad agree, so the mirror
+// within eight lanes (lane 7 - i) supplies lane i ^ 4's value, and after that
+// the mirror within sixteen lanes supplies lane i ^ 8's.  The last two steps
+// combine the four row values (lanes 0, 16, 32, 48) as (R0 + R1) + (R2 + R3),
+// which is what every lane holds after the exchanges with l ^ 16 and l ^ 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float a) {
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false);
+    return a + __int_as_float(t);
 }
 
-// Row totals of the per-block partials part[r][0..nb): one wave per row.
-__device__ __forceinline__ void row_totals(const float *part, float *out, int nrows, int nb,
-                                           int d, bool rstd_step, float eps) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
-    for (int r = wv; r < nrows; r += nwv) {
-        const float *pr = part + r * nb;
-        float a = lane < nb ? pr[lane] : 0.0f;
-        for (int jj = lane + 64; jj < nb; jj += 64) a = a + pr[jj];
-        a = wave_total(a);
-        if (lane == 0) {
-            const float v = a / (float)d;
-            out[r] = rstd_step ? 1.0f / __builtin_sqrtf(v + eps) : v;
+__device__ __forceinline__ float wave_total(float a) {
+    a = dpp_add<0xB1>(a);   // quad_perm [1,0,3,2]: lane l ^ 1
+    a = dpp_add<0x4E>(a);   // quad_perm [2,3,0,1]: lane l ^ 2
+    a = dpp_add<0x141>(a);  // row_half_mirror
+    a = dpp_add<0x140>(a);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Row totals of the block partials part[r][0..nb) for the rows this lane
+// owns (rows g*U .. g*U + U - 1).  Each wave reduces every row any of its
+// lanes needs (all 64 lanes take part; the loops are wave-uniform), so no
+// wave waits for another.
+template <int U>
+__device__ __forceinline__ void own_row_totals(const float *part, int nb, int G, int g, int nrows,
+                                               float (&tot)[U]) {
+    const int lane = threadIdx.x & 63, base = threadIdx.x & ~63;
+    const int g_lo = base / nb, g_top = (base + 63) / nb;
+    const int g_hi = g_top < G - 1 ? g_top : G - 1;
+#pragma unroll
+    for (int k = 0; k < U; ++k) tot[k] = 0.0f;
+    for (int gg = g_lo; gg <= g_hi; ++gg) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int r = gg * U + k;
+            if (r >= nrows) break;
+            const float *pr = part + r * nb;
+            float v = lane < nb ? pr[lane] : 0.0f;
+            for (int jj = lane + 64; jj < nb; jj += 64) v = v + pr[jj];
+            const float t = wave_total(v);
+            if (gg == g) tot[k] = t;
         }
     }
 }
@@ -82,9 +111,8 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     const int d = a.d, nb = a.nb, ROWS = a.G * U;
     float *onep = lds;                  // [d] 1 + scale
     float *shv = lds + d;               // [d] shift
-    float *part = lds + 2 * d;          // [ROWS][nb] block partials
-    float *mean = part + ROWS * nb;     // [ROWS]
-    float *rstd = mean + ROWS;          // [ROWS]
+    float *part = lds + 2 * d;          // [ROWS][nb] block sums
+    float *part2 = part + ROWS * nb;    // [ROWS][nb] block sums of squares
 
     const int s = blockIdx.x / a.wps, w = blockIdx.x - s * a.wps;
     const int64_t row0 = (int64_t)s * a.rps + (int64_t)w * ROWS;
@@ -137,25 +165,27 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
         if (act && r < nrows) part[r * nb + j] = acc;
     }
     __syncthreads();
-    row_totals(part, mean, nrows, nb, d, false, a.eps);
-    __syncthreads();
+    float mu[U];
+    own_row_totals<U>(part, nb, a.G, g, nrows, mu);
 
     // ---- pass 2: centered sums of squares -> 1/sqrt(var + eps) ----
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int r = g * U + k;
-        const float mu = mean[r < nrows ? r : 0];
+        const float m = mu[k] / (float)d;
         float q = 0.0f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
-            z[k][e] = z[k][e] - mu;
+            z[k][e] = z[k][e] - m;
             q = __builtin_fmaf(z[k][e], z[k][e], q);
         }
-        if (act && r < nrows) part[r * nb + j] = q;
+        if (act && r < nrows) part2[r * nb + j] = q;
     }
     __syncthreads();
-    row_totals(part, rstd, nrows, nb, d, true, a.eps);
-    __syncthreads();
+    float rs[U];
+    own_row_totals<U>(part2, nb, a.G, g, nrows, rs);
+#pragma unroll
+    for (int k = 0; k < U; ++k) rs[k] = 1.0f / __builtin_sqrtf(rs[k] / (float)d + a.eps);
 
     // ---- modulate, then transform + quantize (or store bf16 h) ----
     if (!act) return;
@@ -166,12 +196,11 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     for (int k = 0; k < U; ++k) {
         const int r = g * U + k;
         if (r >= nrows) break;
-        const float rs = rstd[r];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const f32x4 o = op4[i], b = sv4[i];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[k][4 * i + e] = __builtin_fmaf(z[k][4 * i + e] * rs, o[e], b[e]);
+            for (int e = 0; e < 4; ++e) z[k][4 * i + e] = __builtin_fmaf(z[k][4 * i + e] * rs[k], o[e], b[e]);
         }
         const int64_t row = row0 + r;
         if (QUANT) {
@@ -194,13 +223,15 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     }
 }
 
-// Rows per thread: 2 by default (the constant setup is shared by two units
-// while the centered values of both stay in registers).
+// Rows per thread: 1 by default.  Two or four rows share the constant setup
+// but hold two or four blocks of centered values in registers (occupancy 3
+// or 2 instead of 7); on 4608 x 3072 one row per thread in workgroups of
+// about 384 threads measured fastest (17.0 us against 20.0 and 25.5 us).
 // KQ_ADALN_ROWS_PER_THREAD (1, 2 or 4; read once) overrides it for sweeps.
 static int adaln_rows_per_thread() {
     static int cached = 0;
     if (cached == 0) {
-        int v = 2;
+        int v = 1;
         const char *e = getenv("KQ_ADALN_ROWS_PER_THREAD");
         if (e) {
             const int q = atoi(e);
@@ -213,13 +244,13 @@ static int adaln_rows_per_thread() {
 
 // Row groups per workgroup: among G with G * nb <= 512 threads, the one whose
 // G * nb threads fill whole waves best; ties go to the G whose workgroup is
-// closest to KQ_ADALN_THREADS threads (default 256, read once; for sweeps).
+// closest to KQ_ADALN_THREADS threads (default 384, read once; for sweeps).
 static int adaln_groups(int nb) {
     static int target = 0;
     if (target == 0) {
         const char *e = getenv("KQ_ADALN_THREADS");
         const int v = e ? atoi(e) : 0;
-        target = v >= 64 && v <= 512 ? v : 256;
+        target = v >= 64 && v <= 512 ? v : 384;
     }
     int best = 1;
     double best_util = -1.0;
@@ -246,7 +277,7 @@ static kq_status launch_adaln(AdalnArgs a, void *stream) {
     const int64_t samples = (a.tokens + a.rps - 1) / a.rps;
     if (wps > INT32_MAX || samples * wps > INT32_MAX) return KQ_ERR_SHAPE;
     a.wps = (int)wps;
-    const size_t lds = sizeof(float) * (2 * (size_t)a.d + (size_t)ROWS * a.nb + 2 * (size_t)ROWS);
+    const size_t lds = sizeof(float) * (2 * (size_t)a.d + 2 * (size_t)ROWS * a.nb);
     auto kern = adaln_kernel<U, QUANT>;
     static bool attr_set = false;
     if (!attr_set) {
