@@ -195,7 +195,8 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
  *   w_codes uint8 [N][K/2] (16-byte aligned), w_scales uint8 [N][K/32] (4-byte aligned)
  *   y       bf16 [M][ld_y], 16-byte aligned, ld_y % 8 == 0, ld_y >= N (written)
  *
- * K % 128 == 0; M and N are arbitrary.  M == 0 or N == 0 returns KQ_OK.
+ * K % 128 == 0; M and N are arbitrary, with max(M, N) * K/2 < 2^31 (one
+ * operand's codes under 2 GiB).  M == 0 or N == 0 returns KQ_OK.
  */
 kq_status kq_w4a4_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
                        const uint8_t *w_codes, const uint8_t *w_scales, int64_t M, int64_t N,

@@ -6,23 +6,31 @@
 // quantizer's layout: codes [rows][K/2] with element k in nibble k%2 of byte
 // k/2, scales [rows][K/32].  For the 32x32x64 FP4 MFMA, lane l holds row l%32
 // and the 32 elements 32*(l/32) .. +31 of a 64-wide K step: exactly one
-// 16-byte chunk of a code row plus its one scale byte, so both operands load
-// from the quantizer's output as is.  The accumulator holds
-// C[8*(r/4) + 4*(l/32) + r%4][l%32] in register r.
+// 16-byte chunk of a code row plus its one scale byte, so both operands come
+// from the quantizer's output as is.
 //
-// Tiling: a workgroup of WM x WN waves computes a (64 WM) x (64 WN) tile of Y,
-// each wave 64 x 64 (2 x 2 MFMA tiles, 64 fp32 accumulators).  K advances in
-// tiles of 128 (two MFMA steps) through double-buffered LDS: the next tile's
-// global loads are issued before the current tile's MFMAs and written to the
-// other buffer after them.  Code rows sit in LDS as four 16-byte chunks with
-// the chunk index XORed by (row >> 1) & 3, so the 32 lanes reading one chunk
-// column of 32 consecutive rows hit distinct banks.  Results go straight from
-// the accumulators to memory as bf16 (nearest even), 64 contiguous bytes per
-// half-wave and accumulator register.
+// The MFMA computes the transposed tile Y^T = W A^T (first operand W): the
+// accumulator register r of lane l then holds Y[m = l%32][n = 8*(r/4) +
+// 4*(l/32) + r%4], four consecutive columns of one output row per group of
+// four registers, which the epilogue stores as 8-byte bf16 quads.
 //
-// The workgroup order is remapped so that each XCD (workgroups go to the 8
-// XCDs round-robin) works on a compact group of M tiles and sweeps the N
-// tiles, which keeps the A rows it shares in its own L2.
+// Tiling: 8 waves (2 along M x 4 along N) compute a 128 x 256 tile of Y, each
+// wave 64 x 64 (2 x 2 MFMA tiles).  K advances in tiles of 256 (four MFMA
+// steps; 128 code bytes and 8 scale bytes per row) through double-buffered
+// LDS: the next tile's global loads are issued before the current tile's
+// MFMAs and written to the other buffer after them.  With one workgroup per
+// CU the wait for those loads is the cost of an iteration, so the K tile is
+// as long as the LDS allows.  All loads are unconditional (clamped indices),
+// so the compiler's memory waits count exactly.  In LDS a code row is eight
+// 16-byte chunks stored at slot c ^ ((row >> 1) & 7): the 16 lanes that one
+// LDS cycle serves read 16 consecutive rows at the same chunk and hit 16
+// distinct slots of a 256-byte bank window.
+//
+// Workgroup order: XCD x (workgroups go to the 8 XCDs round-robin) takes a
+// contiguous range of an order that walks four M tiles for each N tile, so
+// each W tile is fetched into that XCD's L2 once for four workgroups.
+// A K that is a multiple of 128 but not of 256 ends with a half tile whose
+// upper half is zero codes with zero scale bytes (exact zeros in the sum).
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -36,201 +44,206 @@ namespace kq {
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16g __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2g __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 128;          // K elements per LDS tile
-constexpr int kRowBytes = kBK / 2;  // 64 code bytes per row per K tile
+constexpr int kGemmWM = 2, kGemmWN = 4;          // waves along M and N
+constexpr int kBM = 64 * kGemmWM, kBN = 64 * kGemmWN;
+constexpr int kGemmThreads = 64 * kGemmWM * kGemmWN;
+constexpr int kBK = 256;                          // K elements per LDS tile
+constexpr int kRowBytes = kBK / 2;                // 128 code bytes per row per tile
+constexpr int kChunks = kRowBytes / 16;           // 8 chunks of 16 bytes
+constexpr int kMGroup = 4;                        // M tiles that share a W tile
+constexpr int kAB = kBM * kRowBytes, kWB = kBN * kRowBytes;
+constexpr int kScaleSlots = (kBM + kBN + kGemmThreads - 1) / kGemmThreads * kGemmThreads;
+constexpr int kStage = kAB + kWB + 8 * kScaleSlots;  // codes + 8 scale bytes per row slot
+constexpr int kGemmLds = 2 * kStage;
+constexpr int kAPer = kBM * kChunks / kGemmThreads, kWPer = kBN * kChunks / kGemmThreads;
+constexpr int kSPer = kScaleSlots / kGemmThreads;
+static_assert(kBM * kChunks % kGemmThreads == 0 && kBN * kChunks % kGemmThreads == 0, "split");
 
-__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int swz_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int WM, int WN>
-struct GemmShape {
-    static constexpr int BM = 64 * WM, BN = 64 * WN;
-    static constexpr int THREADS = 64 * WM * WN;
-    static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-    static constexpr int STAGE = A_BYTES + B_BYTES + 4 * (BM + BN);  // codes + scale words
-    static constexpr int LDS = 2 * STAGE;
-};
-
-template <int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void w4a4_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldy, int mt_count, int nt_count) {
-    using S = GemmShape<WM, WN>;
+    int M, int N, int K, int64_t ldy, int mtc, int ntc) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-    // ---- workgroup -> (M tile, N tile), XCD-aware ----
-    const int tiles = mt_count * nt_count;
-    const int b = blockIdx.x;
-    const int per_xcd = (tiles + 7) / 8;
-    const int lin = (b % 8) * per_xcd + b / 8;  // XCD x takes a contiguous range
+    // ---- workgroup -> (M tile, N tile) ----
+    const int tiles = mtc * ntc, per = (tiles + 7) / 8;
+    const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (lin >= tiles) return;
-    const int mt = lin / nt_count, nt = lin % nt_count;
-    const int m0 = mt * S::BM, n0 = nt * S::BN;
+    const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
+    const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
+    const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
+    const int m0 = mt * kBM, n0 = nt * kBN;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / kGemmWN, wn = wave % kGemmWN;
     const int i32 = lane & 31, kg = lane >> 5;
-    const int64_t K2 = K / 2, K32 = K / 32;
-    const int KT = K / kBK;
+    const int K2 = K / 2, K32 = K / 32;
+    const int KT = (K + kBK - 1) / kBK;       // the last tile may be a half tile
+    const bool half_tail = (K % kBK) != 0;
 
-    // ---- global -> register staging of one K tile ----
-    constexpr int A_CHUNKS = S::BM * 4, B_CHUNKS = S::BN * 4;  // 16-byte chunks
-    constexpr int A_PER = (A_CHUNKS + S::THREADS - 1) / S::THREADS;
-    constexpr int B_PER = (B_CHUNKS + S::THREADS - 1) / S::THREADS;
-    u32x4 ra[A_PER], rb[B_PER];
-    uint32_t rsa = 0, rsb = 0;
+    // ---- per-thread load plan: byte offsets (rows clamped) and LDS slots ----
+    int ga[kAPer], gw[kWPer], la[kAPer], lw[kWPer], cha[kAPer], chw[kWPer];
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+        const int c = tid + q * kGemmThreads, row = c / kChunks, ch = c % kChunks;
+        const int gr = m0 + row < M ? m0 + row : M - 1;
+        ga[q] = gr * K2 + 16 * ch;
+        la[q] = row * kRowBytes + 16 * swz_slot(row, ch);
+        cha[q] = ch;
+    }
+#pragma unroll
+    for (int q = 0; q < kWPer; ++q) {
+        const int c = tid + q * kGemmThreads, row = c / kChunks, ch = c % kChunks;
+        const int gr = n0 + row < N ? n0 + row : N - 1;
+        gw[q] = gr * K2 + 16 * ch;
+        lw[q] = kAB + row * kRowBytes + 16 * swz_slot(row, ch);
+        chw[q] = ch;
+    }
+    // scale slots: A rows then W rows; slots past BM + BN repeat the last row
+    int gs[kSPer];
+    const uint8_t *sbase[kSPer];
+#pragma unroll
+    for (int q = 0; q < kSPer; ++q) {
+        int v = tid + q * kGemmThreads;
+        v = v < kBM + kBN ? v : kBM + kBN - 1;
+        const int ra = m0 + v < M ? m0 + v : M - 1;
+        const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
+        sbase[q] = v < kBM ? as : ws;
+        gs[q] = (v < kBM ? ra : rw) * K32;
+    }
 
-    auto load_tile = [&](int kt) {
+    struct Regs { u32x4 a[kAPer], w[kWPer]; u32x2g s[kSPer]; };
+    auto gload = [&](int kt, Regs &r) {
+        // in a half tile, chunks 4..7 and scale word 1 re-read the valid
+        // half and are zeroed below
+        const bool half = half_tail && kt == KT - 1;
 #pragma unroll
-        for (int q = 0; q < A_PER; ++q) {
-            const int c = tid + q * S::THREADS;
-            if (c < A_CHUNKS) {
-                int row = m0 + (c >> 2);
-                row = row < M ? row : M - 1;
-                ra[q] = *reinterpret_cast<const u32x4 *>(ac + row * K2 + (int64_t)kt * kRowBytes + 16 * (c & 3));
-            }
+        for (int q = 0; q < kSPer; ++q) {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(sbase[q] + gs[q] + kt * 8);
+            r.s[q] = u32x2g{p[0], p[half ? 0 : 1]};
+            if (half) r.s[q][1] = 0u;
         }
 #pragma unroll
-        for (int q = 0; q < B_PER; ++q) {
-            const int c = tid + q * S::THREADS;
-            if (c < B_CHUNKS) {
-                int row = n0 + (c >> 2);
-                row = row < N ? row : N - 1;
-                rb[q] = *reinterpret_cast<const u32x4 *>(wc + row * K2 + (int64_t)kt * kRowBytes + 16 * (c & 3));
-            }
+        for (int q = 0; q < kAPer; ++q) {
+            const int back = half && cha[q] >= 4 ? 64 : 0;
+            r.a[q] = *reinterpret_cast<const u32x4 *>(ac + ga[q] + kt * kRowBytes - back);
+            if (back) r.a[q] = u32x4{0u, 0u, 0u, 0u};
         }
-        if (tid < S::BM) {
-            int row = m0 + tid;
-            row = row < M ? row : M - 1;
-            rsa = *reinterpret_cast<const uint32_t *>(as + row * K32 + (int64_t)kt * 4);
-        }
-        if (tid < S::BN) {
-            int row = n0 + tid;
-            row = row < N ? row : N - 1;
-            rsb = *reinterpret_cast<const uint32_t *>(ws + row * K32 + (int64_t)kt * 4);
+#pragma unroll
+        for (int q = 0; q < kWPer; ++q) {
+            const int back = half && chw[q] >= 4 ? 64 : 0;
+            r.w[q] = *reinterpret_cast<const u32x4 *>(wc + gw[q] + kt * kRowBytes - back);
+            if (back) r.w[q] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    auto store_tile = [&](int buf) {
-        uint8_t *base = lds + buf * S::STAGE;
+    auto lstore = [&](int buf, const Regs &r) {
+        uint8_t *b = lds + buf * kStage;
 #pragma unroll
-        for (int q = 0; q < A_PER; ++q) {
-            const int c = tid + q * S::THREADS;
-            if (c < A_CHUNKS) {
-                const int row = c >> 2;
-                *reinterpret_cast<u32x4 *>(base + row * kRowBytes + 16 * swz_chunk(row, c & 3)) = ra[q];
-            }
-        }
+        for (int q = 0; q < kAPer; ++q) *reinterpret_cast<u32x4 *>(b + la[q]) = r.a[q];
 #pragma unroll
-        for (int q = 0; q < B_PER; ++q) {
-            const int c = tid + q * S::THREADS;
-            if (c < B_CHUNKS) {
-                const int row = c >> 2;
-                *reinterpret_cast<u32x4 *>(base + S::A_BYTES + row * kRowBytes + 16 * swz_chunk(row, c & 3)) = rb[q];
-            }
-        }
-        uint32_t *sw = reinterpret_cast<uint32_t *>(base + S::A_BYTES + S::B_BYTES);
-        if (tid < S::BM) sw[tid] = rsa;
-        if (tid < S::BN) sw[S::BM + tid] = rsb;
+        for (int q = 0; q < kWPer; ++q) *reinterpret_cast<u32x4 *>(b + lw[q]) = r.w[q];
+        u32x2g *s = reinterpret_cast<u32x2g *>(b + kAB + kWB);
+#pragma unroll
+        for (int q = 0; q < kSPer; ++q) s[tid + q * kGemmThreads] = r.s[q];
     };
 
-    f32x16g acc[2][2];
+    f32x16g acc[2][2];  // [n tile][m tile]
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[r][c] = f32x16g{};
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
 
-    load_tile(0);
-    store_tile(0);
+    auto compute = [&](int buf) {
+        const uint8_t *b = lds + buf * kStage;
+        const uint8_t *s = b + kAB + kWB;  // 8 scale bytes per row slot
+#pragma unroll
+        for (int ks = 0; ks < kBK / 64; ++ks) {
+            const int ch = 2 * ks + kg;  // this lane's 16-byte chunk of the row
+            i32x8 fa[2];
+            int sa[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = wm * 64 + j * 32 + i32;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(b + row * kRowBytes + 16 * swz_slot(row, ch));
+                fa[j] = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+                sa[j] = s[row * 8 + ch];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wn * 64 + i * 32 + i32;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(b + kAB + row * kRowBytes + 16 * swz_slot(row, ch));
+                const i32x8 fw = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+                const int sw = s[(kBM + row) * 8 + ch];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fa[j], acc[i][j], 4, 4,
+                                                                                0, sw, 0, sa[j]);
+            }
+        }
+    };
+
+    Regs r;
+    gload(0, r);
+    lstore(0, r);
     __syncthreads();
-
     for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) load_tile(kt + 1);
-        const uint8_t *base = lds + buf * S::STAGE;
-        const uint32_t *sw = reinterpret_cast<const uint32_t *>(base + S::A_BYTES + S::B_BYTES);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int chunk = 2 * ks + kg;  // this lane's 16-byte chunk of the 64-byte row
-            i32x8 fa[2], fb[2];
-            int sa[2], sb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int ar = wm * 64 + t * 32 + i32;
-                const u32x4 va = *reinterpret_cast<const u32x4 *>(base + ar * kRowBytes + 16 * swz_chunk(ar, chunk));
-                fa[t] = i32x8{(int)va[0], (int)va[1], (int)va[2], (int)va[3], 0, 0, 0, 0};
-                sa[t] = (int)(sw[ar] >> (8 * chunk));
-                const int br = wn * 64 + t * 32 + i32;
-                const u32x4 vb = *reinterpret_cast<const u32x4 *>(base + S::A_BYTES + br * kRowBytes + 16 * swz_chunk(br, chunk));
-                fb[t] = i32x8{(int)vb[0], (int)vb[1], (int)vb[2], (int)vb[3], 0, 0, 0, 0};
-                sb[t] = (int)(sw[S::BM + br] >> (8 * chunk));
-            }
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    acc[r][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[r], fb[c], acc[r][c], 4, 4, 0, sa[r], 0, sb[c]);
-        }
-        if (kt + 1 < KT) store_tile(buf ^ 1);
+        if (kt + 1 < KT) gload(kt + 1, r);
+        compute(kt & 1);
+        if (kt + 1 < KT) lstore((kt + 1) & 1, r);
         __syncthreads();
     }
 
-    // ---- epilogue: bf16, rounded to nearest even; for each accumulator
-    // register the 32 lanes of a half-wave write 64 contiguous bytes of a row ----
+    // ---- epilogue: bf16 (nearest even), four columns of a row per store ----
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int j = 0; j < 2; ++j) {
+        const int row = m0 + wm * 64 + j * 32 + i32;
+        if (row >= M) continue;
+        uint16_t *yr = y + (int64_t)row * ldy;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int col = n0 + wn * 64 + c * 32 + i32;
+        for (int i = 0; i < 2; ++i) {
+            const int cb = n0 + wn * 64 + i * 32 + 4 * kg;
 #pragma unroll
-            for (int q = 0; q < 16; q += 2) {
-                const int row = m0 + wm * 64 + r * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
-                const uint32_t h = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(f32x2{acc[r][c][q], acc[r][c][q + 1]}, bf16x2));
-                if (col < N) {
-                    if (row < M) y[(int64_t)row * ldy + col] = (uint16_t)(h & 0xffffu);
-                    if (row + 1 < M) y[(int64_t)(row + 1) * ldy + col] = (uint16_t)(h >> 16);
+            for (int q = 0; q < 4; ++q) {
+                const int col = cb + 8 * q;
+                const uint32_t lo = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
+                const uint32_t hi = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
+                if (col + 3 < N) {
+                    *reinterpret_cast<u32x2g *>(yr + col) = u32x2g{lo, hi};
+                } else {
+                    if (col < N) yr[col] = (uint16_t)(lo & 0xffffu);
+                    if (col + 1 < N) yr[col + 1] = (uint16_t)(lo >> 16);
+                    if (col + 2 < N) yr[col + 2] = (uint16_t)(hi & 0xffffu);
                 }
             }
         }
-}
-
-static int gemm_variant() {
-    static int cached = 0;
-    if (cached == 0) {
-        int v = 24;
-        const char *e = getenv("KQ_GEMM_WAVES");  // WM*10 + WN: 22, 24, 42 or 44
-        if (e) {
-            int q = atoi(e);
-            if (q == 22 || q == 24 || q == 42 || q == 44) v = q;
-        }
-        cached = v;
     }
-    return cached;
 }
 
-template <int WM, int WN>
 static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t *wc,
                              const uint8_t *ws, uint16_t *y, int M, int N, int K, int64_t ldy,
                              void *stream) {
-    using S = GemmShape<WM, WN>;
-    const int mtc = (M + S::BM - 1) / S::BM, ntc = (N + S::BN - 1) / S::BN;
-    const int tiles = mtc * ntc;
-    const int grid = ((tiles + 7) / 8) * 8;
+    const int mtc = (M + kBM - 1) / kBM, ntc = (N + kBN - 1) / kBN;
+    const int64_t tiles = (int64_t)mtc * ntc;
+    const int64_t grid = (tiles + 7) / 8 * 8;
+    if (grid > INT32_MAX) return KQ_ERR_SHAPE;
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
-    const void *fn = (const void *)w4a4_gemm_kernel<WM, WN>;
+    const void *fn = (const void *)w4a4_gemm_kernel;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS) != hipSuccess)
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds) != hipSuccess)
             return KQ_ERR_HIP;
         attr_set = true;
     }
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(S::THREADS), args, S::LDS,
-                                   (hipStream_t)stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args,
+                                         kGemmLds, (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
@@ -242,20 +255,16 @@ extern "C" kq_status kq_w4a4_gemm(const uint8_t *a_codes, const uint8_t *a_scale
                                   const uint8_t *w_codes, const uint8_t *w_scales, int64_t M,
                                   int64_t N, int64_t K, void *y, int64_t ld_y, void *stream) {
     if (M < 0 || N < 0 || K < 0 || M >= (int64_t(1) << 30) || N >= (int64_t(1) << 30) ||
-        K >= (int64_t(1) << 24) || K % kBK != 0 || ld_y < N)
+        K >= (int64_t(1) << 24) || K % 128 != 0 || ld_y < N)
         return KQ_ERR_SHAPE;
     if (M == 0 || N == 0) return KQ_OK;
     if (K == 0) return KQ_ERR_SHAPE;
+    // byte offsets inside an operand are 32-bit
+    if ((M > N ? M : N) * (K / 2) >= (int64_t(1) << 31)) return KQ_ERR_SHAPE;
     if (!a_codes || !a_scales || !w_codes || !w_scales || !y) return KQ_ERR_NULL;
     if (((uintptr_t)a_codes % 16) || ((uintptr_t)w_codes % 16) || ((uintptr_t)a_scales % 4) ||
         ((uintptr_t)w_scales % 4) || ((uintptr_t)y % 16) || (ld_y % 8))
         return KQ_ERR_ALIGN;
-    const int m = (int)M, n = (int)N, k = (int)K;
-    uint16_t *yp = (uint16_t *)y;
-    switch (gemm_variant()) {
-        case 22: return launch_gemm<2, 2>(a_codes, a_scales, w_codes, w_scales, yp, m, n, k, ld_y, stream);
-        case 24: return launch_gemm<2, 4>(a_codes, a_scales, w_codes, w_scales, yp, m, n, k, ld_y, stream);
-        case 42: return launch_gemm<4, 2>(a_codes, a_scales, w_codes, w_scales, yp, m, n, k, ld_y, stream);
-        default: return launch_gemm<4, 4>(a_codes, a_scales, w_codes, w_scales, yp, m, n, k, ld_y, stream);
-    }
+    return launch_gemm(a_codes, a_scales, w_codes, w_scales, (uint16_t *)y, (int)M, (int)N, (int)K,
+                       ld_y, stream);
 }

@@ -103,6 +103,7 @@ def test_parameter_pointer_checks():
     assert g(A16, A16, None, A16, 8, 16, 128, A16, 16) == kq.KQ_ERR_NULL
     assert g(A16, A16 + 2, A16, A16, 8, 16, 128, A16, 16) == kq.KQ_ERR_ALIGN
     assert g(A16, A16, A16, A16, 8, 16, 128, A16 + 2, 16) == kq.KQ_ERR_ALIGN
+    assert g(A16, A16, A16, A16, 1 << 20, 16, 4096, A16, 16) == kq.KQ_ERR_SHAPE  # 2 GiB operand
 
 
 def test_adaln_argument_checks():
