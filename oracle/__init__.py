@@ -61,6 +61,8 @@ _SIGS = {
                                          _P, _INT, _P, _P, _INT]),
     "kqo_adaln_bound": (_INT, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                _INT]),
+    "kqo_calib_objective": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _INT]),
+    "kqo_calib_es_update": (None, [_I64, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -392,3 +394,29 @@ def adaln_bound(x_bits, shift, scale, lu, rows_per_sample=None, eps=1e-6, d=None
                                float(eps), _ptr(lu), _ptr(bound), threads or default_threads())
     _check(rc, "kqo_adaln_bound")
     return bound
+
+
+# ---- calibration of the block parameters -------------------------------------
+def calib_objective(x_bits, lu, gram=None, d=None, threads=None) -> np.ndarray:
+    """Per-block f_j = sum_t r G_j r^T of the MXFP4 round trip (fp64 [nb])."""
+    x_bits, tokens, d, ld = _x_args(x_bits, d)
+    lu = _lu_arg(lu, d)
+    f = np.zeros(d // 32, np.float64)
+    g = None
+    if gram is not None:
+        g = np.ascontiguousarray(gram, np.float32)
+        assert g.shape == (d // 32, 32, 32)
+    rc = lib().kqo_calib_objective(_ptr(x_bits), tokens, d, ld, _ptr(lu),
+                                   _ptr(g) if g is not None else None, _ptr(f),
+                                   threads or default_threads())
+    _check(rc, "kqo_calib_objective")
+    return f
+
+
+def calib_es_update(theta, sigma, fbest, cand, fcand, noise):
+    """One (1+1)-ES step on float32 arrays, in place (theta, sigma, fbest, cand)."""
+    nb = sigma.shape[0]
+    for a in (theta, sigma, fbest, cand, fcand, noise):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"]
+    lib().kqo_calib_es_update(nb, _ptr(theta), _ptr(sigma), _ptr(fbest), _ptr(cand), _ptr(fcand),
+                              _ptr(noise))

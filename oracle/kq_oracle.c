@@ -934,3 +934,100 @@ int kqo_adaln_bound(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
     parallel_rows(row_adaln_bound, &c, tokens, threads);
     return 0;
 }
+
+/* ======================================================================== */
+/* Calibration of the block parameters ([KQ-sum] "Approach": the factors     */
+/* are learned layer-wise from the Hadamard start with an output loss)       */
+/* ======================================================================== */
+/*
+ * Objective of block j over a calibration set:
+ *   f_j = sum_t r_t G_j r_t^T,  r_t = dequant(MXFP4(x_t T_j)) T_j^-1 - x_t,
+ * x_t the block's 32 values of token t, G_j a 32x32 weighting (the identity
+ * when gram is NULL: the round-trip error of the quantizer; W_j^T W_j for the
+ * block-diagonal part of the output error of X W^T).  The MXFP4 decisions are
+ * taken on the fixed-fp32-order transform (the kernel's values); the decoded
+ * values, the inverse (adjugate Kronecker factors) and the sums are fp64.
+ * A block whose scale byte is NaN makes f_j NaN.
+ */
+typedef struct {
+    const uint16_t *x;
+    int64_t tokens, d, ld;
+    const float *lu, *gram;
+    double *f;
+} cal_ctx;
+
+static void block_objective(void *vc, int64_t j) {
+    const cal_ctx *c = (const cal_ctx *)vc;
+    const float *p = c->lu + j * 15;
+    double Ti[1024];
+    kqo_block_inverse_matrix(p, Ti);
+    const float *G = c->gram ? c->gram + j * 1024 : NULL;
+    double acc = 0.0;
+    for (int64_t t = 0; t < c->tokens; ++t) {
+        float xb[32], yb[32];
+        const uint16_t *src = c->x + t * c->ld + j * 32;
+        for (int i = 0; i < 32; ++i) xb[i] = kqo_bf16_to_f32(src[i]);
+        kqo_block_transform_staged32(xb, p, yb);
+        uint8_t codes[16], sbyte;
+        kqo_mxfp4_block(yb, codes, &sbyte);
+        const double sc = kqo_e8m0_value(sbyte);
+        double q[32], r[32];
+        for (int k = 0; k < 32; ++k) {
+            const uint8_t code = (codes[k / 2] >> (4 * (k & 1))) & 0xF;
+            q[k] = kqo_e2m1_value(code) * sc;
+        }
+        for (int i = 0; i < 32; ++i) {
+            double v = 0.0;
+            for (int k = 0; k < 32; ++k) v += q[k] * Ti[k * 32 + i];
+            r[i] = v - (double)xb[i];
+        }
+        double e = 0.0;
+        if (G) {
+            for (int a = 0; a < 32; ++a)
+                for (int b = 0; b < 32; ++b) e += r[a] * (double)G[a * 32 + b] * r[b];
+        } else {
+            for (int a = 0; a < 32; ++a) e += r[a] * r[a];
+        }
+        acc += e;
+    }
+    c->f[j] = acc;
+}
+
+int kqo_calib_objective(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                        const float *lu, const float *gram, double *f, int threads) {
+    if (!x || !lu || !f || bad_shape(tokens, d, ld)) return -1;
+    cal_ctx c = {x, tokens, d, ld, lu, gram, f};
+    parallel_rows(block_objective, &c, d / 32, threads);
+    return 0;
+}
+
+/*
+ * One step of the per-block (1+1) evolution strategy with the 1/5 success
+ * rule (all fp32, in this order):
+ *   if fcand < fbest:  theta = cand, fbest = fcand, sigma = min(sigma * 1.5, 0.5)
+ *   else:              sigma = max(sigma * 0.90360200 (= 1.5^-1/4), 1e-4)
+ *   cand = fma(sigma, noise, theta) per parameter; if any u (parameter 3b+1)
+ *   of cand has |u| < 0.1, cand = theta (no move: the next comparison fails).
+ */
+void kqo_calib_es_update(int64_t nb, float *theta, float *sigma, float *fbest, float *cand,
+                         const float *fcand, const float *noise) {
+    for (int64_t j = 0; j < nb; ++j) {
+        float *th = theta + j * 15, *cd = cand + j * 15;
+        const float *nz = noise + j * 15;
+        if (fcand[j] < fbest[j]) {
+            memcpy(th, cd, 15 * sizeof(float));
+            fbest[j] = fcand[j];
+            const float s = sigma[j] * 1.5f;
+            sigma[j] = s < 0.5f ? s : 0.5f;
+        } else {
+            const float s = sigma[j] * 0.90360200f;
+            sigma[j] = s > 1e-4f ? s : 1e-4f;
+        }
+        int ok = 1;
+        for (int i = 0; i < 15; ++i) {
+            cd[i] = fmaf(sigma[j], nz[i], th[i]);
+            if (i % 3 == 1 && fabsf(cd[i]) < 0.1f) ok = 0;
+        }
+        if (!ok) memcpy(cd, th, 15 * sizeof(float));
+    }
+}

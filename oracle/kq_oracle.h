@@ -165,6 +165,18 @@ int kqo_adaln_bound(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
                     const float *shift, const float *scale, int64_t rows_per_sample, float eps,
                     const float *lu, double *bound, int threads);
 
+/* Calibration of the block parameters ([KQ-sum] "Approach": learned from the
+ * Hadamard start with an output loss).  Per block j over the calibration
+ * tokens: f_j = sum_t r_t G_j r_t^T with r_t = dequant(MXFP4(x_t T_j)) T_j^-1
+ * - x_t; G_j = identity when gram is NULL (fp32 [nb][32][32] otherwise).  The
+ * MXFP4 decisions use the fixed-fp32-order transform; the rest is fp64. */
+int kqo_calib_objective(const uint16_t *x, int64_t tokens, int64_t d, int64_t ld,
+                        const float *lu, const float *gram, double *f, int threads);
+/* One step of the per-block (1+1) evolution strategy with the 1/5 success
+ * rule; see kq_oracle.c for the exact fp32 operations. */
+void kqo_calib_es_update(int64_t nb, float *theta, float *sigma, float *fbest, float *cand,
+                         const float *fcand, const float *noise);
+
 /* Y[m][n] = sum_k A[m][k] * W[n][k] in fp64 (A, W fp32 row-major). */
 int kqo_matmul_nt(const float *A, const float *W, int64_t M, int64_t N, int64_t K,
                   double *Y, int threads);
