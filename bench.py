@@ -75,6 +75,7 @@ KERNEL_MATCH = {
     "kq_w4a4_gemm": "w4a4_gemm_kernel",
     "kq_adaln_transform_quant": "adaln_kernelILi1ELb1E",
     "kq_adaln_modulate": "adaln_kernelILi1ELb0E",
+    "kq_calib_objective": "calib_objective_kernel",
 }
 
 PROFILE_COMMANDS = """\
@@ -394,6 +395,31 @@ def main() -> int:
         extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
                                   "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
                                   "fused_speedup": round(ums / fms, 3)}
+    if not args.no_peers and d == 3072:
+        # Calibration of the block parameters from the Hadamard start (per-block
+        # (1+1)-ES on the MXFP4 round-trip objective): 150 iterations on 256
+        # rows, then the round-trip error on 256 held-out rows.
+        xa = inputs.activation(args.workload)
+        cal, held = xs[0][:256], torch.from_numpy(xa[2048:2304].view(np.int16)).view(torch.bfloat16).to(dev)
+        start = torch.from_numpy(inputs.hadamard_init(nb)).to(dev)
+        noise = torch.from_numpy(inputs.calib_noise(args.workload, 150)).to(dev)
+        kq.calibrate(cal, start, noise[:3])  # warm
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        theta, _, _ = kq.calibrate(cal, start, noise)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        xh = inputs.bf16_bits_to_f32(xa[2048:2304]).astype(np.float64)
+        energy = float((xh ** 2).sum())
+        f0 = kq.calib_objective(held, start).double().sum().item()
+        f1 = kq.calib_objective(held, theta).double().sum().item()
+        extra["calibration"] = {
+            "iterations": 150, "calibration_rows": 256, "held_out_rows": 256,
+            "ms_per_iteration": round(c0.elapsed_time(c1) / 150, 4),
+            "held_out_rel_err_hadamard": round((f0 / energy) ** 0.5, 5),
+            "held_out_rel_err_calibrated": round((f1 / energy) ** 0.5, 5)}
     if gemm:
         timed("kq_transform_quant", R, 0)  # A operands: fresh quantizer outputs
         pms = timed("kq_weight_quant", max(10, args.steps // 10), max(2, args.warmup // 10))

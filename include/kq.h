@@ -245,6 +245,42 @@ kq_status kq_adaln_modulate(const void *x, int64_t tokens, int64_t d, int64_t ld
                             float eps, void *h, int64_t ld_h, void *stream);
 
 /*
+ * kq_calib_objective — calibration objective of every block (KroQuant
+ * summary, "Approach": the factors are learned layer-wise from the Hadamard
+ * start with an output loss; the loss and optimiser are not given, so this
+ * library takes the quantizer's own error):
+ *   f_j = sum_t r_t G_j r_t^T,  r_t = dequant(MXFP4(x_t T_j)) T_j^-1 - x_t,
+ * over the tokens of a calibration set, x_t the 32 values of block j.
+ *
+ *   x      bf16 [tokens][ld_x], as for kq_transform_quant
+ *   lu     fp32 [d/32][5][3], the parameters to score (one candidate per block)
+ *   gram   fp32 [d/32][32][32] weighting G_j, or NULL for the identity (the
+ *          round-trip error); W_j^T W_j gives the block-diagonal part of the
+ *          output error of X W^T
+ *   f      fp32 [d/32] (written)
+ *
+ * The MXFP4 decisions and both transforms follow the quantizer's fixed fp32
+ * orders; per-thread fp32 sums are reduced in a fixed order, so the value is
+ * reproducible bit for bit.  tokens == 0 writes zeros.
+ */
+kq_status kq_calib_objective(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                             const float *lu, const float *gram, float *f, void *stream);
+
+/*
+ * kq_calib_es_update — one step of the per-block (1+1) evolution strategy
+ * with the 1/5 success rule, on device arrays (fp32, in place):
+ *   theta [nb][15] kept parameters, sigma [nb] step sizes, fbest [nb] kept
+ *   objectives, cand [nb][15] the candidate just scored (replaced by the next
+ *   one), fcand [nb] its objective, noise [nb][15] standard normal draws.
+ * If fcand < fbest the candidate is kept and sigma grows by 1.5 (at most 0.5);
+ * otherwise sigma shrinks by 1.5^-1/4 = 0.90360200 (at least 1e-4).  The next
+ * candidate is fma(sigma, noise, theta), or theta itself when any u would
+ * fall within 0.1 of zero.
+ */
+kq_status kq_calib_es_update(int64_t nb, float *theta, float *sigma, float *fbest, float *cand,
+                             const float *fcand, const float *noise, void *stream);
+
+/*
  * kq_copy_ceiling — not a quantizer: moves the same bytes as
  * kq_transform_quant (reads the bf16 tensor, writes d/2 + d/32 bytes per row)
  * with almost no arithmetic, to measure the achievable bandwidth of this

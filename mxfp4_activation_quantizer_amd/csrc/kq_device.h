@@ -92,4 +92,26 @@ __device__ __forceinline__ void mxfp4_block(const float (&y)[32], u32x4 &codes,
     sbyte = s;
 }
 
+// MXFP4 decode of one block: 16 code bytes (4 dwords of 8 codes, element 0 in
+// the low nibble) times 2^(s-127) by the gfx950 scaled convert; a NaN scale
+// byte makes the whole block NaN.
+__device__ __forceinline__ void mxfp4_decode(const u32x4 &c, uint32_t s, float (&z)[32]) {
+    const float scale = __uint_as_float(s << 23);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], scale, 0);
+        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], scale, 1);
+        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], scale, 2);
+        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], scale, 3);
+        z[8 * q + 0] = v0[0]; z[8 * q + 1] = v0[1];
+        z[8 * q + 2] = v1[0]; z[8 * q + 3] = v1[1];
+        z[8 * q + 4] = v2[0]; z[8 * q + 5] = v2[1];
+        z[8 * q + 6] = v3[0]; z[8 * q + 7] = v3[1];
+    }
+    if (s == 255u) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) z[k] = __builtin_nanf("");
+    }
+}
+
 }  // namespace kq

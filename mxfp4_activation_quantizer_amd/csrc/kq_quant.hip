@@ -83,88 +83,13 @@ struct Mxfp4Src {
         r.s = scales[unit];
     }
     __device__ __forceinline__ static void unpack(const Raw &r, float (&z)[32]) {
-        const float scale = __uint_as_float(r.s << 23);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 0);
-            const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 1);
-            const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 2);
-            const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[q], scale, 3);
-            z[8 * q + 0] = v0[0]; z[8 * q + 1] = v0[1];
-            z[8 * q + 2] = v1[0]; z[8 * q + 3] = v1[1];
-            z[8 * q + 4] = v2[0]; z[8 * q + 5] = v2[1];
-            z[8 * q + 6] = v3[0]; z[8 * q + 7] = v3[1];
-        }
-        if (r.s == 255u) {
-#pragma unroll
-            for (int k = 0; k < 32; ++k) z[k] = __builtin_nanf("");
-        }
+        mxfp4_decode(r.c, r.s, z);
     }
 };
 
 // ---------------------------------------------------------------------------
 // Transform stages.
 // ---------------------------------------------------------------------------
-
-// Inverse of the block transform: T^-1 = (D_4 (x)...(x) D_0)^-1 (G_4 (x)...(x) G_0)^-1
-// (the inverse of y = x * T, KroQuant abstract: "invertible" transform, its
-// inverse applied to the weights).  First z_k = y_k * e_k with e_k the running
-// product over b = 0..4 of (bit b of k ? u_b : 1/u_b); then bits b = 4..0 map
-// each pair (r, s) back by q = s - w*r, p = r - l*q (two fused multiply-adds).
-// Constants shared by the inverse and the weight-side stages: l_b, w_b and
-// e_k = running product over b = 0..4 of (bit b of k ? u_b : 1/u_b), the
-// diagonal of (D_4 (x)...(x) D_0)^-1.
-struct KronInvConsts {
-    const float *lu;
-    float p[15];
-    float l[5], w[5], ek[32];
-    __device__ __forceinline__ void fetch(int j) {
-        const float *src = lu + (int64_t)j * 15;
-#pragma unroll
-        for (int i = 0; i < 15; ++i) p[i] = src[i];
-    }
-    __device__ __forceinline__ void setup() {
-        float u[5], iu[5];
-#pragma unroll
-        for (int b = 0; b < 5; ++b) {
-            l[b] = p[3 * b + 0];
-            u[b] = p[3 * b + 1];
-            w[b] = u[b] * p[3 * b + 2];
-            iu[b] = rcp_rn(u[b]);
-        }
-        ek[0] = iu[0];
-        ek[1] = u[0];
-#pragma unroll
-        for (int b = 1; b < 5; ++b) {
-            const int h = 1 << b;
-#pragma unroll
-            for (int k = 0; k < h; ++k) {
-                ek[k + h] = ek[k] * u[b];
-                ek[k] = ek[k] * iu[b];
-            }
-        }
-    }
-};
-
-struct KronInverseStage : KronInvConsts {
-    __device__ __forceinline__ void apply(float (&z)[32]) const {
-#pragma unroll
-        for (int k = 0; k < 32; ++k) z[k] = z[k] * ek[k];
-#pragma unroll
-        for (int b = 4; b >= 0; --b) {
-            const int h = 1 << b;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                if (i & h) continue;
-                const float r = z[i], s = z[i | h];
-                const float q = __builtin_fmaf(-w[b], r, s);
-                const float pv = __builtin_fmaf(-l[b], q, r);
-                z[i] = pv;
-                z[i | h] = q;
-            }
-        }
-    }
-};
 
 // Weight side of the invariance (X T)(W T^-T)^T = X W^T (LRQ-DiT Sec. 3.2
 // Eq. (2) with an invertible T; KroQuant abstract: the inverse goes to the

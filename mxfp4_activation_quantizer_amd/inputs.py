@@ -185,6 +185,15 @@ def modulation(name: str, samples: int = 1, d: int | None = None):
     return shift, scale
 
 
+def calib_noise(name: str, iterations: int, blocks: int | None = None) -> np.ndarray:
+    """Standard normal draws for the calibration's evolution strategy,
+    float32 [iterations + 1][blocks][15]."""
+    w = WORKLOADS[name]
+    blocks = w.blocks if blocks is None else blocks
+    g = rng(w.wid, 4)
+    return g.standard_normal((iterations + 1, blocks, 15)).astype(np.float32)
+
+
 def gemm_weight() -> np.ndarray:
     """W4A4 consumer weights W [N=12288][K=3072] ~ N(0, 0.02), bf16 bits."""
     g = rng(GEMM_WID, 0)

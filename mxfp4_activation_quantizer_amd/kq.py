@@ -44,6 +44,8 @@ SIGNATURES = {
                                        _P, _P, _P]),
     "kq_adaln_modulate": (_ST, [_P, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64,
                                 _P]),
+    "kq_calib_objective": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kq_calib_es_update": (_ST, [_I64, _P, _P, _P, _P, _P, _P, _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -136,6 +138,14 @@ def kq_adaln_modulate(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps, h,
                       stream=None) -> int:
     return lib().kq_adaln_modulate(x, tokens, d, ld_x, shift, scale, rows_per_sample, eps, h, ld_h,
                                    stream)
+
+
+def kq_calib_objective(x, tokens, d, ld_x, lu, gram, f, stream=None) -> int:
+    return lib().kq_calib_objective(x, tokens, d, ld_x, lu, gram, f, stream)
+
+
+def kq_calib_es_update(nb, theta, sigma, fbest, cand, fcand, noise, stream=None) -> int:
+    return lib().kq_calib_es_update(nb, theta, sigma, fbest, cand, fcand, noise, stream)
 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
@@ -315,3 +325,47 @@ def adaln_modulate(x, shift, scale, rows_per_sample=None, eps: float = 1e-6,
         x.data_ptr(), tokens, d, ld, shift.data_ptr(), scale.data_ptr(),
         _rps(tokens, rows_per_sample), float(eps), h.data_ptr(), h.stride(0), _stream(x)))
     return h
+
+
+def calib_objective(x, lu, gram=None, d: int | None = None, f=None):
+    """fp32 [d/32] per-block MXFP4 round-trip objective of parameters ``lu``."""
+    torch = _torch()
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    if f is None:
+        f = torch.empty(d // 32, dtype=torch.float32, device=x.device)
+    _check("kq_calib_objective", kq_calib_objective(
+        x.data_ptr(), tokens, d, ld, lu.data_ptr(), gram.data_ptr() if gram is not None else None,
+        f.data_ptr(), _stream(x)))
+    return f
+
+
+def calibrate(x, lu0, noise, gram=None, sigma0: float = 0.05):
+    """Per-block (1+1)-ES calibration of the block parameters on the tokens of
+    ``x`` (bf16 GPU [tokens][d]), starting from ``lu0`` (fp32 [d/32][5][3]).
+
+    ``noise`` is a float32 GPU tensor [iterations + 1][d/32][15] of standard
+    normal draws (the first proposes the first candidate).  Each iteration is
+    two launches: kq_calib_objective on the candidates, kq_calib_es_update.
+    Returns (theta [d/32][5][3], fbest [d/32], history [iterations + 1][d/32])."""
+    torch = _torch()
+    nb = lu0.shape[0]
+    iters = noise.shape[0] - 1
+    theta = lu0.reshape(nb, 15).clone().contiguous()
+    cand = theta.clone()
+    sigma = torch.full((nb,), sigma0, dtype=torch.float32, device=x.device)
+    fbest = calib_objective(x, theta, gram)
+    history = torch.empty((iters + 1, nb), dtype=torch.float32, device=x.device)
+    history[0].copy_(fbest)
+    fcand = torch.full((nb,), float("inf"), dtype=torch.float32, device=x.device)
+    st = _stream(x)
+    _check("kq_calib_es_update", kq_calib_es_update(
+        nb, theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
+        fcand.data_ptr(), noise[0].data_ptr(), st))
+    for i in range(iters):
+        calib_objective(x, cand, gram, f=fcand)
+        _check("kq_calib_es_update", kq_calib_es_update(
+            nb, theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
+            fcand.data_ptr(), noise[i + 1].data_ptr(), st))
+        history[i + 1].copy_(fbest)
+    return theta.reshape(nb, 5, 3), fbest, history

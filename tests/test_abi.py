@@ -137,6 +137,26 @@ def test_adaln_argument_checks():
     assert m(*ok, A16, 68) == kq.KQ_ERR_ALIGN
 
 
+def test_calibration_argument_checks():
+    o = kq.kq_calib_objective
+    assert o(A16, 4, 48, 64, A16, None, A16) == kq.KQ_ERR_SHAPE      # d % 32
+    assert o(A16, 4, 64, 32, A16, None, A16) == kq.KQ_ERR_SHAPE      # ld < d
+    assert o(A16, -1, 64, 64, A16, None, A16) == kq.KQ_ERR_SHAPE
+    assert o(None, 4, 64, 64, A16, None, A16) == kq.KQ_ERR_NULL
+    assert o(A16, 4, 64, 64, None, None, A16) == kq.KQ_ERR_NULL
+    assert o(A16, 4, 64, 64, A16, None, None) == kq.KQ_ERR_NULL
+    assert o(ODD, 4, 64, 64, A16, None, A16) == kq.KQ_ERR_ALIGN
+    assert o(A16, 4, 64, 68, A16, None, A16) == kq.KQ_ERR_ALIGN
+    assert o(A16, 4, 64, 64, A16 + 2, None, A16) == kq.KQ_ERR_ALIGN
+    assert o(A16, 4, 64, 64, A16, A16 + 1, A16) == kq.KQ_ERR_ALIGN
+    u = kq.kq_calib_es_update
+    assert u(0, None, None, None, None, None, None) == kq.KQ_OK
+    assert u(-1, A16, A16, A16, A16, A16, A16) == kq.KQ_ERR_SHAPE
+    assert u(4, None, A16, A16, A16, A16, A16) == kq.KQ_ERR_NULL
+    assert u(4, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_NULL
+    assert u(4, A16, A16 + 2, A16, A16, A16, A16) == kq.KQ_ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
