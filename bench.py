@@ -40,7 +40,7 @@ CSRC = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
 
 # The files the quantizer kernel is built from: a counter summary stays valid
 # until one of them changes.
-QUANT_SOURCES = ("kq_quant.hip", "kq_device.h", "Makefile")
+QUANT_SOURCES = ("kq_quant.hip", "kq_kron.h", "kq_device.h", "Makefile")
 
 
 def kernel_source_hash() -> str:
@@ -73,9 +73,10 @@ KERNEL_MATCH = {
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
     "kq_w4a4_gemm": "w4a4_gemm_kernel",
-    "kq_adaln_transform_quant": "adaln_kernelILi1ELb1E",
-    "kq_adaln_modulate": "adaln_kernelILi1ELb0E",
+    "kq_adaln_transform_quant": "adaln_kernel<1, true>",
+    "kq_adaln_modulate": "adaln_kernel<1, false>",
     "kq_calib_objective": "calib_objective_kernel",
+    "kq_calib_es_update": "calib_es_update_kernel",
 }
 
 PROFILE_COMMANDS = """\
@@ -130,6 +131,10 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                     rate = f"{gemm_flops / (avg * 1e6):10.1f} TFLOP/s ({w.tokens}x{inputs.GEMM_N}x{inputs.GEMM_K})"
                 elif entry == "kq_weight_quant":
                     rate = f"{weight_bytes / (avg * 1e3):10.1f} ({inputs.GEMM_N}x{inputs.GEMM_K} weight)"
+                elif entry == "kq_adaln_modulate":
+                    rate = f"{4 * w.elements / (avg * 1e3):10.1f} (bf16 in, bf16 out)"
+                elif entry.startswith("kq_calib"):
+                    rate = f"{'':>10s} (one candidate set, 256 x {w.d} calibration rows)"
                 else:
                     rate = f"{nbytes / (avg * 1e3):10.1f}"
                 lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
@@ -244,6 +249,7 @@ def main() -> int:
     R = max(2, -(-2 * MALL_BYTES // set_bytes))
     x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    x_keep = x0.clone() if not (args.kernel_only or args.no_peers) else None
     codes = [torch.empty((T, d // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
     scales = [torch.empty((T, nb), dtype=torch.uint8, device=dev) for _ in range(R)]
     lu_d = torch.from_numpy(lu).to(dev)
@@ -386,6 +392,11 @@ def main() -> int:
             extra[name] = {"ms_per_step": round(pms, 6),
                            "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+        # the copy ceiling and the inverse wrote into the rotating buffers:
+        # restore the inputs before the next peers read them
+        for xi in xs:
+            xi.copy_(x_keep)
+        timed("kq_transform_quant", R, 0)
         # AdaLN + quantizer: fused (one pass, same bytes as the quantizer) vs
         # modulate-to-bf16 then quantize (4 more bytes per element through HBM)
         fms = timed("kq_adaln_transform_quant", args.steps, args.warmup)
@@ -400,7 +411,8 @@ def main() -> int:
         # (1+1)-ES on the MXFP4 round-trip objective): 150 iterations on 256
         # rows, then the round-trip error on 256 held-out rows.
         xa = inputs.activation(args.workload)
-        cal, held = xs[0][:256], torch.from_numpy(xa[2048:2304].view(np.int16)).view(torch.bfloat16).to(dev)
+        cal = torch.from_numpy(xa[:256].view(np.int16)).view(torch.bfloat16).to(dev)
+        held = torch.from_numpy(xa[2048:2304].view(np.int16)).view(torch.bfloat16).to(dev)
         start = torch.from_numpy(inputs.hadamard_init(nb)).to(dev)
         noise = torch.from_numpy(inputs.calib_noise(args.workload, 150)).to(dev)
         kq.calibrate(cal, start, noise[:3])  # warm

@@ -615,3 +615,20 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     _log(f"W4A4 end-to-end rel. error vs X W^T (KroQuant, random params): {rel:.4f}")
     assert rel < 0.5
+    # the baselines through the same consumer: FWHT32 (H orthonormal and
+    # symmetric, so the weights take W H as well) and per-channel scaling
+    # (weights W diag(1/mult)); all on the GPU with the library's kernels
+    wd = to_gpu_bf16(w)
+    fa = kq.fwht32_quant(xd)
+    fw = kq.fwht32_quant(wd)
+    mult = inputs.smooth_multipliers(x)
+    sa = kq.smooth_quant(xd, to_gpu(mult))
+    sw = kq.smooth_quant(wd, to_gpu((1.0 / mult.astype(np.float64)).astype(np.float32)))
+    errs = {}
+    for name, (a_, w_) in {"fwht32": (fa, fw), "smooth": (sa, sw)}.items():
+        yy = kq.w4a4_gemm(a_[0], a_[1], w_[0], w_[1])
+        gy = inputs.bf16_bits_to_f32(_np(yy.view(torch.int16)).view(np.uint16)[rows]).astype(np.float64)
+        errs[name] = np.linalg.norm(gy - ref) / np.linalg.norm(ref)
+    _log("W4A4 end-to-end rel. error vs X W^T: " +
+         ", ".join(f"{k} {v:.4f}" for k, v in errs.items()))
+    assert all(v < 0.5 for v in errs.values())
