@@ -432,6 +432,8 @@ def main() -> int:
             "ms_per_iteration": round(c0.elapsed_time(c1) / 150, 4),
             "held_out_rel_err_hadamard": round((f0 / energy) ** 0.5, 5),
             "held_out_rel_err_calibrated": round((f1 / energy) ** 0.5, 5)}
+        if gemm:
+            gemm["theta"] = theta
     if gemm:
         timed("kq_transform_quant", R, 0)  # A operands: fresh quantizer outputs
         pms = timed("kq_weight_quant", max(10, args.steps // 10), max(2, args.warmup // 10))
@@ -439,6 +441,32 @@ def main() -> int:
                                  "GBps": round(gemm["weight_bytes"] / (pms * 1e-3) / 1e9, 1)}
         pms = timed("kq_w4a4_gemm", max(10, args.steps // 10), max(2, args.warmup // 10))
         tf = gemm["flops"] / (pms * 1e-3) / 1e12
+        if "theta" in gemm:
+            # end-to-end error of W4A4 against the unquantised X W^T on 24
+            # sampled rows, for each transform through the same consumer
+            xa = inputs.activation(args.workload)
+            wa = inputs.gemm_weight()
+            rows = np.sort(np.random.default_rng(9).choice(T, 24, replace=False))
+            ref = inputs.bf16_bits_to_f32(xa[rows]).astype(np.float64) @ \
+                inputs.bf16_bits_to_f32(wa).astype(np.float64).T
+            xdev = torch.from_numpy(xa.view(np.int16)).view(torch.bfloat16).to(dev)
+            mult = inputs.smooth_multipliers(xa)
+            minv = torch.from_numpy((1.0 / mult.astype(np.float64)).astype(np.float32)).to(dev)
+            multd = torch.from_numpy(mult).to(dev)
+            pairs = {
+                "kron_calibrated": (kq.transform_quant(xdev, gemm["theta"]),
+                                    kq.weight_quant(gemm["w"], gemm["theta"])),
+                "kron_random_params": (kq.transform_quant(xdev, lu_d), kq.weight_quant(gemm["w"], lu_d)),
+                "fwht32": (kq.fwht32_quant(xdev), kq.fwht32_quant(gemm["w"])),
+                "smooth": (kq.smooth_quant(xdev, multd), kq.smooth_quant(gemm["w"], minv)),
+            }
+            e2e = {}
+            for name_, ((ac_, as__), (wc_, ws_)) in pairs.items():
+                yy = kq.w4a4_gemm(ac_, as__, wc_, ws_)
+                got = inputs.bf16_bits_to_f32(
+                    yy.view(torch.int16).cpu().numpy().view(np.uint16)[rows]).astype(np.float64)
+                e2e[name_] = round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 5)
+            extra["w4a4_end_to_end_rel_err"] = e2e
         extra["w4a4_gemm"] = {"ms_per_step": round(pms, 6), "shape_mnk": [T, gemm["n"], gemm["k"]],
                               "TFLOPs": round(tf, 1), "peak_TFLOPs": PEAK_FP4_TFLOPS,
                               "frac": round(tf / PEAK_FP4_TFLOPS, 4)}

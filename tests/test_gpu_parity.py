@@ -629,6 +629,15 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
         yy = kq.w4a4_gemm(a_[0], a_[1], w_[0], w_[1])
         gy = inputs.bf16_bits_to_f32(_np(yy.view(torch.int16)).view(np.uint16)[rows]).astype(np.float64)
         errs[name] = np.linalg.norm(gy - ref) / np.linalg.norm(ref)
+    # the Kronecker transform with parameters calibrated on 256 other rows
+    cal_rows = np.setdiff1d(np.arange(256), rows)[:256]
+    theta, _, _ = kq.calibrate(to_gpu_bf16(x[cal_rows]), to_gpu(inputs.hadamard_init(96)),
+                               to_gpu(inputs.calib_noise("flux_attn", 150)))
+    ca = kq.transform_quant(xd, theta)
+    cw = kq.weight_quant(wd, theta)
+    yy = kq.w4a4_gemm(ca[0], ca[1], cw[0], cw[1])
+    gy = inputs.bf16_bits_to_f32(_np(yy.view(torch.int16)).view(np.uint16)[rows]).astype(np.float64)
+    errs["kron_calibrated"] = np.linalg.norm(gy - ref) / np.linalg.norm(ref)
     _log("W4A4 end-to-end rel. error vs X W^T: " +
          ", ".join(f"{k} {v:.4f}" for k, v in errs.items()))
     assert all(v < 0.5 for v in errs.values())
