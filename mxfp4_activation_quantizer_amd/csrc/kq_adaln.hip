@@ -126,7 +126,7 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     const bool act = g < a.G;
 
     // ---- parameters, then this thread's U units, then the sample vectors ----
-    KronStage ks{a.lu, {}, {}, {}};
+    KronStage ks = KronStage::from(a.lu);
     if (QUANT) ks.fetch(j);
     u32x4 raw[U][4];
 #pragma unroll

@@ -47,9 +47,8 @@ __global__ __launch_bounds__(kCalThreads) void calib_objective_kernel(
     if (gram) {
         for (int i = tid; i < 1024; i += kCalThreads) G[i] = gram[(int64_t)j * 1024 + i];
     }
-    KronStage fw{lu, {}, {}, {}, {}};
-    KronInverseStage iv;
-    iv.lu = lu;
+    KronStage fw = KronStage::from(lu);
+    KronInverseStage iv = KronInverseStage::from(lu);
     fw.fetch(j);
     iv.fetch(j);
     fw.setup();

@@ -15,6 +15,12 @@ namespace kq {
 // bit, then one multiply per element by d_k = prod_b (bit b of k ? 1/u_b : u_b).
 struct KronStage {
     const float *lu;  // [nb][5][3]
+    // kernels take only the parameter pointer and build the lane state here
+    __device__ __forceinline__ static KronStage from(const float *p) {
+        KronStage s;
+        s.lu = p;
+        return s;
+    }
     float p[15];      // raw (l, u, v) x 5 of this lane's block
     float l[5], w[5], dk[32];
     __device__ __forceinline__ void fetch(int j) {
@@ -103,6 +109,11 @@ struct KronInvConsts {
 };
 
 struct KronInverseStage : KronInvConsts {
+    __device__ __forceinline__ static KronInverseStage from(const float *p) {
+        KronInverseStage s;
+        s.lu = p;
+        return s;
+    }
     __device__ __forceinline__ void apply(float (&z)[32]) const {
 #pragma unroll
         for (int k = 0; k < 32; ++k) z[k] = z[k] * ek[k];

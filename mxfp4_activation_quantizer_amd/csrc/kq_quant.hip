@@ -97,6 +97,11 @@ struct Mxfp4Src {
 // G^-T = [[1,-l],[0,1]] [[1,0],[-w,1]]: each pair (p, q) on bit b = 0..4 maps
 // to s = q - l*p, r = p - w*s, then every element is multiplied by e_k.
 struct KronWeightStage : KronInvConsts {
+    __device__ __forceinline__ static KronWeightStage from(const float *p) {
+        KronWeightStage s;
+        s.lu = p;
+        return s;
+    }
     __device__ __forceinline__ void apply(float (&z)[32]) const {
 #pragma unroll
         for (int b = 0; b < 5; ++b) {
@@ -119,6 +124,11 @@ struct KronWeightStage : KronInvConsts {
 // Per-channel scaling baseline: y_c = x_c * mult_c.
 struct SmoothStage {
     const float *mult;  // [d]
+    __device__ __forceinline__ static SmoothStage from(const float *p) {
+        SmoothStage s;
+        s.mult = p;
+        return s;
+    }
     float m[32];
     __device__ __forceinline__ void fetch(int j) {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(mult + (int64_t)j * 32);
@@ -139,6 +149,7 @@ struct SmoothStage {
 // Orthonormal 32-point Walsh-Hadamard (Sylvester order, LRQ-DiT Eq. (3)):
 // five add/subtract stages, then one multiply by fl32(1/sqrt(32)).
 struct FwhtStage {
+    __device__ __forceinline__ static FwhtStage from(const float *) { return FwhtStage{}; }
     __device__ __forceinline__ void fetch(int) {}
     __device__ __forceinline__ void setup() {}
     __device__ __forceinline__ void apply(float (&z)[32]) const {
@@ -160,6 +171,7 @@ struct FwhtStage {
 };
 
 struct IdentityStage {
+    __device__ __forceinline__ static IdentityStage from(const float *) { return IdentityStage{}; }
     __device__ __forceinline__ void fetch(int) {}
     __device__ __forceinline__ void setup() {}
     __device__ __forceinline__ void apply(float (&)[32]) const {}
@@ -243,12 +255,28 @@ struct FoldSink {
 // repeat their last unit (same bytes to the same place), so no lane branches.
 // ---------------------------------------------------------------------------
 template <class Src, class Stage, class Sink, int NU>
-__global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, Stage stage, Sink sink,
+__global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const float *stage_param,
+                                                              Sink sink,
                                                               int tokens, int nb, int tstep) {
+    Stage stage = Stage::from(stage_param);
     const int g = blockIdx.x * kBlockThreads + threadIdx.x;
     const int j = g % nb;
     const int t0 = g / nb;
     if (t0 >= tokens) return;
+    if constexpr (NU == 1) {
+        // one unit per lane: no unit count or clamping (saves an integer
+        // division per lane)
+        stage.fetch(j);
+        typename Src::Raw r;
+        src.load(t0, j, r);
+        __builtin_amdgcn_sched_barrier(0);
+        stage.setup();
+        float z[32];
+        Src::unpack(r, z);
+        stage.apply(z);
+        sink.store(t0, j, z);
+        return;
+    }
     const int avail = (tokens - 1 - t0) / tstep + 1;
     const int cnt = avail < NU ? avail : NU;
     const int last = t0 + (cnt - 1) * tstep;
@@ -343,7 +371,7 @@ static kq_status launch(Kernel kernel, const Plan &pl, void *stream, Args... arg
 }
 
 template <class Src, class Stage, class Sink>
-static kq_status run(const Src &src, const Stage &stage, const Sink &sink, int64_t tokens, int nb,
+static kq_status run(const Src &src, const float *stage, const Sink &sink, int64_t tokens, int nb,
                      void *stream) {
     Plan pl;
     if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
@@ -399,8 +427,8 @@ kq_status kq_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t l
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     if (!aligned(lu, 4)) return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    return run(Bf16Src{(const uint16_t *)x, ld_x}, KronStage{lu, {}, {}, {}},
-               Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+    return run<Bf16Src, KronStage>(Bf16Src{(const uint16_t *)x, ld_x}, lu,
+                                   Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
 }
 
 kq_status kq_transform_f32(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
@@ -410,8 +438,8 @@ kq_status kq_transform_f32(const void *x, int64_t tokens, int64_t d, int64_t ld_
     if (!lu || !y) return KQ_ERR_NULL;
     if (!aligned(lu, 4) || !aligned(y, 16)) return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    return run(Bf16Src{(const uint16_t *)x, ld_x}, KronStage{lu, {}, {}, {}}, F32Sink{y, d},
-               tokens, nb, stream);
+    return run<Bf16Src, KronStage>(Bf16Src{(const uint16_t *)x, ld_x}, lu, F32Sink{y, d}, tokens,
+                                   nb, stream);
 }
 
 kq_status kq_smooth_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
@@ -422,7 +450,7 @@ kq_status kq_smooth_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     if (!aligned(mult, 16)) return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    return run(Bf16Src{(const uint16_t *)x, ld_x}, SmoothStage{mult, {}},
+    return run<Bf16Src, SmoothStage>(Bf16Src{(const uint16_t *)x, ld_x}, mult,
                Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
 }
 
@@ -432,7 +460,7 @@ kq_status kq_fwht32_quant(const void *x, int64_t tokens, int64_t d, int64_t ld_x
     if (st != KQ_OK || tokens == 0) return st;
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     const int nb = (int)(d / 32);
-    return run(Bf16Src{(const uint16_t *)x, ld_x}, FwhtStage{}, Mxfp4Sink{codes, scales, nb},
+    return run<Bf16Src, FwhtStage>(Bf16Src{(const uint16_t *)x, ld_x}, nullptr, Mxfp4Sink{codes, scales, nb},
                tokens, nb, stream);
 }
 
@@ -444,7 +472,8 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     if (!aligned(y, 16) || (ld_y * 4) % 16 != 0) return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    return run(F32Src{y, ld_y}, IdentityStage{}, Mxfp4Sink{codes, scales, nb}, tokens, nb, stream);
+    return run<F32Src, IdentityStage>(F32Src{y, ld_y}, nullptr, Mxfp4Sink{codes, scales, nb}, tokens,
+                                      nb, stream);
 }
 
 kq_status kq_weight_quant(const void *w, int64_t rows, int64_t k, int64_t ld_w,
@@ -455,10 +484,8 @@ kq_status kq_weight_quant(const void *w, int64_t rows, int64_t k, int64_t ld_w,
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     if (!aligned(lu, 4)) return KQ_ERR_ALIGN;
     const int nb = (int)(k / 32);
-    KronWeightStage stage;
-    stage.lu = lu;
-    return run(Bf16Src{(const uint16_t *)w, ld_w}, stage, Mxfp4Sink{codes, scales, nb}, rows,
-               nb, stream);
+    return run<Bf16Src, KronWeightStage>(Bf16Src{(const uint16_t *)w, ld_w}, lu,
+                                         Mxfp4Sink{codes, scales, nb}, rows, nb, stream);
 }
 
 kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
@@ -470,10 +497,8 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
     if (!aligned(codes, 16) || !aligned(x_out, 16) || (ld_out * 2) % 16 != 0 || !aligned(lu, 4))
         return KQ_ERR_ALIGN;
     const int nb = (int)(d / 32);
-    KronInverseStage stage;
-    stage.lu = lu;
-    return run(Mxfp4Src{codes, scales, nb}, stage,
-               Bf16Sink{(uint16_t *)x_out, ld_out}, tokens, nb, stream);
+    return run<Mxfp4Src, KronInverseStage>(Mxfp4Src{codes, scales, nb}, lu,
+                                           Bf16Sink{(uint16_t *)x_out, ld_out}, tokens, nb, stream);
 }
 
 kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
@@ -482,7 +507,7 @@ kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x
     if (st != KQ_OK || tokens == 0) return st;
     if ((st = check_mxfp4_out(codes, scales)) != KQ_OK) return st;
     const int nb = (int)(d / 32);
-    return run(Bf16Src{(const uint16_t *)x, ld_x}, IdentityStage{}, FoldSink{codes, scales, nb},
+    return run<Bf16Src, IdentityStage>(Bf16Src{(const uint16_t *)x, ld_x}, nullptr, FoldSink{codes, scales, nb},
                tokens, nb, stream);
 }
 
