@@ -37,6 +37,13 @@
 
 namespace kq {
 
+// LDS position (in 16-B chunks) of chunk i (0..7) of block j's 32-float
+// slice of a sample vector.  Lane j reads its block's eight chunks with a
+// 128-B stride between lanes; XOR-ing the chunk index with bits 1..3 of j
+// spreads any 16 consecutive lanes over all 64 banks (no conflicts), and the
+// staging writes, eight consecutive chunks per block, stay conflict-free.
+__device__ __forceinline__ int vec_chunk(int j, int i) { return j * 8 + (i ^ ((j >> 1) & 7)); }
+
 constexpr int kAdalnMaxD = 8192;  // the modulation vectors of one sample live in LDS
                                   // (and d/32 <= 256 fits one 512-thread workgroup)
 
@@ -105,12 +112,16 @@ __device__ __forceinline__ void own_row_totals(const float *part, int nb, int G,
     }
 }
 
+// bf16 form: the wave exchange runs in four rounds of 16 units (1.1 KB of LDS
+// per wave next to the sample vectors; one round of 64 measured slower).
+constexpr int kModRounds = 4;
+
 template <int U, bool QUANT>
 __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     extern __shared__ float lds[];
     const int d = a.d, nb = a.nb, ROWS = a.G * U;
-    float *onep = lds;                  // [d] 1 + scale
-    float *shv = lds + d;               // [d] shift
+    float *onep = lds;                  // [d] 1 + scale (chunks placed by vec_chunk)
+    float *shv = lds + d;               // [d] shift (chunks placed by vec_chunk)
     float *part = lds + 2 * d;          // [ROWS][nb] block sums
     float *part2 = part + ROWS * nb;    // [ROWS][nb] block sums of squares
 
@@ -142,8 +153,9 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
         const f32x4 *sh4 = reinterpret_cast<const f32x4 *>(a.shift + (int64_t)s * d);
         for (int i = tid; i < d / 4; i += blockDim.x) {
             const f32x4 c = sc4[i], b = sh4[i];
-            reinterpret_cast<f32x4 *>(onep)[i] = f32x4{1.0f + c[0], 1.0f + c[1], 1.0f + c[2], 1.0f + c[3]};
-            reinterpret_cast<f32x4 *>(shv)[i] = b;
+            const int at = vec_chunk(i >> 3, i & 7);
+            reinterpret_cast<f32x4 *>(onep)[at] = f32x4{1.0f + c[0], 1.0f + c[1], 1.0f + c[2], 1.0f + c[3]};
+            reinterpret_cast<f32x4 *>(shv)[at] = b;
         }
     }
 
@@ -188,17 +200,19 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     for (int k = 0; k < U; ++k) rs[k] = 1.0f / __builtin_sqrtf(rs[k] / (float)d + a.eps);
 
     // ---- modulate, then transform + quantize (or store bf16 h) ----
-    if (!act) return;
+    // The bf16 form stores through the wave exchange, so every lane of a
+    // wave stays to the end (lanes without a row store nothing).
+    if (QUANT && !act) return;
     if (QUANT) ks.setup();
-    const f32x4 *op4 = reinterpret_cast<const f32x4 *>(onep + j * 32);
-    const f32x4 *sv4 = reinterpret_cast<const f32x4 *>(shv + j * 32);
+    const f32x4 *op4 = reinterpret_cast<const f32x4 *>(onep);
+    const f32x4 *sv4 = reinterpret_cast<const f32x4 *>(shv);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int r = g * U + k;
-        if (r >= nrows) break;
+        if (QUANT && r >= nrows) break;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const f32x4 o = op4[i], b = sv4[i];
+            const f32x4 o = op4[vec_chunk(j, i)], b = sv4[vec_chunk(j, i)];
 #pragma unroll
             for (int e = 0; e < 4; ++e) z[k][4 * i + e] = __builtin_fmaf(z[k][4 * i + e] * rs[k], o[e], b[e]);
         }
@@ -212,13 +226,13 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
             __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(a.codes) + unit);
             __builtin_nontemporal_store((uint8_t)sb, a.scales + unit);
         } else {
+            __shared__ WaveStoreBuf<kModRounds> wsb[512 / 64];
             uint32_t hw[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m)
                 hw[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{z[k][2 * m], z[k][2 * m + 1]}, bf16x2));
-            u32x4 *p = reinterpret_cast<u32x4 *>(a.h + row * a.ldh + (int64_t)j * 32);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = u32x4{hw[4 * i], hw[4 * i + 1], hw[4 * i + 2], hw[4 * i + 3]};
+            const bool valid = act && r < nrows;
+            wave_store64(wsb[tid >> 6], hw, valid ? (void *)(a.h + row * a.ldh + (int64_t)j * 32) : nullptr);
         }
     }
 }

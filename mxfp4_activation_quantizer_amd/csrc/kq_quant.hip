@@ -181,6 +181,7 @@ struct IdentityStage {
 // Sinks: what is stored per unit.
 // ---------------------------------------------------------------------------
 struct Mxfp4Sink {
+    static constexpr bool kWave = false;
     uint8_t *codes;   // [tokens][d/2]
     uint8_t *scales;  // [tokens][nb]
     int nb;
@@ -194,23 +195,27 @@ struct Mxfp4Sink {
     }
 };
 
-// bf16 output, rounded to nearest even by the hardware pack-convert.
+// bf16 output, rounded to nearest even by the hardware pack-convert, and
+// stored whole-line through the wave exchange (kWave: every lane of a wave
+// calls store, lanes without a unit with valid == false).
 struct Bf16Sink {
+    static constexpr bool kWave = true;
     uint16_t *x;  // [tokens][ld]
     int64_t ld;
-    __device__ __forceinline__ void store(int t, int j, const float (&z)[32]) const {
+    __device__ __forceinline__ void store(int t, int j, const float (&z)[32], bool valid) const {
+        __shared__ WaveStoreBuf<1> buf[kBlockThreads / 64];
         uint32_t w[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             w[m] = __builtin_bit_cast(uint32_t,
                                       __builtin_convertvector(f32x2{z[2 * m], z[2 * m + 1]}, bf16x2));
-        u32x4 *p = reinterpret_cast<u32x4 *>(x + (int64_t)t * ld + (int64_t)j * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        wave_store64(buf[threadIdx.x >> 6], w,
+                     valid ? (void *)(x + (int64_t)t * ld + (int64_t)j * 32) : nullptr);
     }
 };
 
 struct F32Sink {
+    static constexpr bool kWave = false;
     float *y;  // [tokens][d]
     int64_t d;
     __device__ __forceinline__ void store(int t, int j, const float (&z)[32]) const {
@@ -224,6 +229,7 @@ struct F32Sink {
 // the XOR of the unit's fp32 bit patterns eight at a time, the scale byte the
 // low byte of their XOR.  Same loads, same stores, almost no arithmetic.
 struct FoldSink {
+    static constexpr bool kWave = false;
     uint8_t *codes;
     uint8_t *scales;
     int nb;
@@ -261,8 +267,24 @@ __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const flo
     Stage stage = Stage::from(stage_param);
     const int g = blockIdx.x * kBlockThreads + threadIdx.x;
     const int j = g % nb;
-    const int t0 = g / nb;
-    if (t0 >= tokens) return;
+    int t0 = g / nb;
+    bool valid = true;
+    if constexpr (Sink::kWave) {
+        // the wave stores together: only a wave wholly past the end leaves;
+        // its other lanes past the end redo the last row's unit and store
+        // nothing
+        if ((g & ~63) / nb >= tokens) return;
+        if (t0 >= tokens) {
+            valid = false;
+            t0 = tokens - 1;
+        }
+    } else {
+        if (t0 >= tokens) return;
+    }
+    auto put = [&](int t, const float (&z)[32]) {
+        if constexpr (Sink::kWave) sink.store(t, j, z, valid);
+        else sink.store(t, j, z);
+    };
     if constexpr (NU == 1) {
         // one unit per lane: no unit count or clamping (saves an integer
         // division per lane)
@@ -274,7 +296,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const flo
         float z[32];
         Src::unpack(r, z);
         stage.apply(z);
-        sink.store(t0, j, z);
+        put(t0, z);
         return;
     }
     const int avail = (tokens - 1 - t0) / tstep + 1;
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const flo
         float z[32];
         Src::unpack(buf[k], z);
         stage.apply(z);
-        sink.store(k < cnt ? t0 + k * tstep : last, j, z);
+        put(k < cnt ? t0 + k * tstep : last, z);
     }
 }
 

@@ -496,6 +496,24 @@ def test_dequant_inverse_ragged(torch_cuda, tokens, nb):
     _inverse_vs_definition(c, s, lu, got)
 
 
+@pytest.mark.parametrize("tokens,nb,pad", [(5, 3, 8), (70, 1, 24), (131, 7, 16)])
+def test_dequant_inverse_strided_output_leaves_padding(torch_cuda, tokens, nb, pad):
+    """Row stride beyond d: every unit lands at its row's offset (the stores
+    go out whole-line through a wave exchange, units of a wave spanning
+    several rows) and the padding columns keep their sentinel."""
+    torch = torch_cuda
+    g = np.random.default_rng(tokens * 31 + nb)
+    x = inputs.f64_to_bf16_bits(g.standard_normal((tokens, nb * 32)) * 2)
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    c, s = _gpu_tq(x, lu)
+    d = nb * 32
+    out = torch.full((tokens, d + pad), -7.0, dtype=torch.bfloat16, device="cuda")
+    kq.dequant_inverse(to_gpu(c), to_gpu(s), to_gpu(lu), x_out=out[:, :d])
+    got = _np(out.view(torch.int16)).view(np.uint16)
+    np.testing.assert_array_equal(got[:, :d], oracle.dequant_inverse(c, s, lu, oracle.STAGED32))
+    assert (inputs.bf16_bits_to_f32(got[:, d:]) == -7.0).all()
+
+
 def test_round_trip_error_flux_mlp(torch_cuda):
     """FLUX-MLP-shaped input: quantise then dequantise+invert on the GPU; the
     relative Frobenius error of the Kron path is reported next to the
