@@ -12,7 +12,8 @@
 // The MFMA computes the transposed tile Y^T = W A^T (first operand W): the
 // accumulator register r of lane l then holds Y[m = l%32][n = 8*(r/4) +
 // 4*(l/32) + r%4], four consecutive columns of one output row per group of
-// four registers, which the epilogue stores as 8-byte bf16 quads.
+// four registers; the epilogue gathers the bf16 tile in LDS and stores it a
+// whole row at a time.
 //
 // Tiling: 8 waves (2 along M x 4 along N) compute a 128 x 256 tile of Y, each
 // wave 64 x 64 (2 x 2 MFMA tiles).  K advances in tiles of 256 (four MFMA
@@ -198,30 +199,49 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
         __syncthreads();
     }
 
-    // ---- epilogue: bf16 (nearest even), four columns of a row per store ----
+    // ---- epilogue: bf16 (nearest even) through LDS, whole rows per store ----
+    // Written straight from the accumulators, each store instruction would
+    // put 16 bytes into each of 32 rows (a line completed over eight
+    // instructions), which halves HBM write throughput.  The tile goes to
+    // LDS first (free after the loop's last barrier): element (r, c) sits in
+    // 8-byte slot (c / 4) ^ (r & 31) of a 512-byte row, so the 32 rows one
+    // accumulator store touches hit 32 distinct slots of a bank window.
+    // Then each thread stores 16 bytes = 8 columns of one row: a wave writes
+    // two whole 512-byte tile rows per instruction.
+    static_assert(kBM * kBN * 2 <= kGemmLds, "the output tile fits the LDS");
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int row = m0 + wm * 64 + j * 32 + i32;
-        if (row >= M) continue;
-        uint16_t *yr = y + (int64_t)row * ldy;
+        const int row = wm * 64 + j * 32 + i32;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int cb = n0 + wn * 64 + i * 32 + 4 * kg;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = cb + 8 * q;
+                const int s8 = wn * 16 + i * 8 + 2 * q + kg;  // (column / 4) in the tile
                 const uint32_t lo = __builtin_bit_cast(
                     uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
                 const uint32_t hi = __builtin_bit_cast(
                     uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
-                if (col + 3 < N) {
-                    *reinterpret_cast<u32x2g *>(yr + col) = u32x2g{lo, hi};
-                } else {
-                    if (col < N) yr[col] = (uint16_t)(lo & 0xffffu);
-                    if (col + 1 < N) yr[col + 1] = (uint16_t)(lo >> 16);
-                    if (col + 2 < N) yr[col + 2] = (uint16_t)(hi & 0xffffu);
-                }
+                *reinterpret_cast<u32x2g *>(lds + row * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
             }
+        }
+    }
+    __syncthreads();
+    constexpr int kRowChunks = kBN * 2 / 16;  // 16-byte chunks per tile row
+#pragma unroll
+    for (int k = 0; k < kBM * kRowChunks / kGemmThreads; ++k) {
+        const int f = tid + k * kGemmThreads;
+        const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * (kBN * 2) + 16 * (ch ^ (g >> 1)));
+        if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int gr = m0 + row, col = n0 + 8 * ch;
+        if (gr >= M || col >= N) continue;
+        uint16_t *yp = y + (int64_t)gr * ldy + col;
+        if (col + 7 < N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
         }
     }
 }

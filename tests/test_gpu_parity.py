@@ -608,6 +608,23 @@ def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     _assert_gemm_close(yb, Y, B, K)
 
 
+@pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8)])
+def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
+    """Row stride beyond N: the whole-row epilogue writes only columns < N
+    of rows < M; the padding keeps its sentinel."""
+    torch = torch_cuda
+    g = np.random.default_rng(M + 3 * N + K)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    ld = (N + pad + 7) // 8 * 8
+    buf = torch.full((M, ld), 5.0, dtype=torch.bfloat16, device="cuda")
+    kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws), y=buf[:, :N])
+    yb = _np(buf.view(torch.int16)).view(np.uint16)
+    Y, B = _gemm_reference(ac, as_, wc, ws)
+    _assert_gemm_close(yb[:, :N], Y, B, K)
+    assert (inputs.bf16_bits_to_f32(yb[:, N:]) == 5.0).all()
+
+
 def test_gemm_full_size_sampled_rows(torch_cuda):
     """4608 x 12288 x 3072, the FLUX attention-projection consumer: quantizer
     output times prepared weights; 24 sampled rows checked against the fp64
