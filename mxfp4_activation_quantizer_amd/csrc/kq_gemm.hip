@@ -246,6 +246,238 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS form: the same tiles, waves, MFMAs and epilogue, but the
+// operand tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4 for codes, _dword for scales) through three LDS
+// stages, so two K tiles are in flight while a third is multiplied and no
+// registers hold them on the way.  A DMA lane writes 16 bytes at (stage
+// base + 16 * lane), so the XOR slot layout is made on the global side: the
+// lane that lands in slot s of a row fetches chunk s ^ ((row >> 1) & 7).
+// Waits are explicit: before tile kt is read, vmcnt(one tile's DMAs) retires
+// tile kt's DMAs and leaves tile kt + 1's in flight; the barrier after it
+// also tells every wave that the stage of tile kt - 1 is free, and the DMAs
+// of tile kt + 2 go into that stage.  The stages are three separate LDS
+// arrays, so the compiler sees that the pending DMAs (into the other two)
+// do not alias the reads and adds no waits of its own.
+// ---------------------------------------------------------------------------
+constexpr int kDScale = 8 * (kBM + kBN);         // 8 scale bytes per A and W row
+constexpr int kDStage = kAB + kWB + kDScale;     // 52224 bytes
+constexpr int kDA = kAB / 1024 / (kGemmThreads / 64);     // A DMAs (1 KB per wave) per wave
+constexpr int kDW = kWB / 1024 / (kGemmThreads / 64);     // W DMAs per wave
+constexpr int kDSRegions = kDScale / 256;                 // 256-byte scale regions
+constexpr int kDS = (kDSRegions + kGemmThreads / 64 - 1) / (kGemmThreads / 64);
+constexpr int kDPerTile = kDA + kDW + kDS;                // DMAs per thread per K tile
+static_assert(kAB % (1024 * (kGemmThreads / 64)) == 0 && kWB % (1024 * (kGemmThreads / 64)) == 0,
+              "whole 1 KB regions per wave");
+static_assert(kDPerTile < 16, "vmcnt immediate");
+
+__shared__ __attribute__((aligned(16))) uint8_t gemm_st0[kDStage];
+__shared__ __attribute__((aligned(16))) uint8_t gemm_st1[kDStage];
+__shared__ __attribute__((aligned(16))) uint8_t gemm_st2[kDStage];
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
+}
+// s_waitcnt with vmcnt(n) and no expcnt / lgkmcnt wait (gfx9 encoding)
+#define KQ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// This lane's DMA sources (byte offsets at K tile 0) and, per DMA, whether
+// a half tile has no data there.
+struct DmaPlan {
+    int ga[kDA], gw[kDW], gs[kDS], rs[kDS];
+    bool hia[kDA], hiw[kDW], his[kDS];
+    const uint8_t *sb[kDS];
+};
+
+// Tile kt of both operands into stage st.  The restrict parameter gives the
+// DMAs alias-scope metadata once inlined, which lets the compiler's wait
+// insertion tell the stages apart.
+__device__ __forceinline__ void gemm_issue(const DmaPlan &pl, const uint8_t *ac, const uint8_t *wc,
+                                           int kt, bool half, int wave, uint8_t *__restrict__ st) {
+#pragma unroll
+    for (int q = 0; q < kDA; ++q)
+        dma16(ac + pl.ga[q] + kt * kRowBytes - (half && pl.hia[q] ? 64 : 0),
+              st + (q * (kGemmThreads / 64) + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < kDW; ++q)
+        dma16(wc + pl.gw[q] + kt * kRowBytes - (half && pl.hiw[q] ? 64 : 0),
+              st + kAB + (q * (kGemmThreads / 64) + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < kDS; ++q)
+        dma4(pl.sb[q] + pl.gs[q] + kt * 8 - (half && pl.his[q] ? 4 : 0), st + kAB + kWB + pl.rs[q] * 256);
+}
+
+// nks K steps of 64 from stage b into the wave's 2 x 2 accumulator tiles.
+__device__ __forceinline__ void gemm_compute(const uint8_t *__restrict__ b, int nks, int wm, int wn,
+                                             int i32, int kg, f32x16g (&acc)[2][2]) {
+    const uint8_t *sc = b + kAB + kWB;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 64; ++ks) {
+        if (ks >= nks) break;
+        const int ch = 2 * ks + kg;
+        i32x8 fa[2];
+        int sa[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = wm * 64 + j * 32 + i32;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(b + row * kRowBytes + 16 * swz_slot(row, ch));
+            fa[j] = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+            sa[j] = sc[row * 8 + ch];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = wn * 64 + i * 32 + i32;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(b + kAB + row * kRowBytes + 16 * swz_slot(row, ch));
+            const i32x8 fw = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+            const int sw = sc[(kBM + row) * 8 + ch];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fa[j], acc[i][j], 4, 4, 0,
+                                                                            sw, 0, sa[j]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_dma_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
+    const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldy, int mtc, int ntc) {
+    // ---- workgroup -> (M tile, N tile), as in w4a4_gemm_kernel ----
+    const int tiles = mtc * ntc, per = (tiles + 7) / 8;
+    const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (lin >= tiles) return;
+    const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
+    const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
+    const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
+    const int m0 = mt * kBM, n0 = nt * kBN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kGemmWN, wn = wave % kGemmWN;
+    const int i32 = lane & 31, kg = lane >> 5;
+    const int K2 = K / 2, K32 = K / 32;
+    const int KT = (K + kBK - 1) / kBK;
+    const bool half_tail = (K % kBK) != 0;
+
+    // ---- DMA plan: source offsets of this lane, one region per DMA ----
+    DmaPlan pl;
+#pragma unroll
+    for (int q = 0; q < kDA; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the A tile
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
+        pl.hia[q] = c >= 4;
+    }
+#pragma unroll
+    for (int q = 0; q < kDW; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
+        pl.hiw[q] = c >= 4;
+    }
+#pragma unroll
+    for (int q = 0; q < kDS; ++q) {
+        int r = q * (kGemmThreads / 64) + wave;
+        r = r < kDSRegions ? r : r - (kGemmThreads / 64);  // past the last: a repeat
+        pl.rs[q] = r;
+        const int dw = r * 64 + lane, v = dw >> 1, hf = dw & 1;  // row slot, dword of its 8 bytes
+        const int ra = m0 + v < M ? m0 + v : M - 1;
+        const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
+        pl.sb[q] = v < kBM ? as : ws;
+        pl.gs[q] = (v < kBM ? ra : rw) * K32 + 4 * hf;
+        pl.his[q] = hf;
+    }
+
+    auto issue = [&](int kt, uint8_t *st) {
+        gemm_issue(pl, ac, wc, kt, half_tail && kt == KT - 1, wave, st);
+    };
+
+    f32x16g acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
+
+    auto compute = [&](const uint8_t *b, int kt) {
+        gemm_compute(b, half_tail && kt == KT - 1 ? 2 : kBK / 64, wm, wn, i32, kg, acc);
+    };
+
+    // ---- three stages: step s issues tile s and multiplies tile s - 2 ----
+    // Step s: vmcnt(one tile) retires tile s - 2 (tile s - 1 stays in
+    // flight); the barrier makes every wave's DMAs of tile s - 2 visible and
+    // frees the stage of tile s - 3, which takes tile s.  Steps past the last
+    // tile issue a repeat of it (never read).  The compiler's wait insertion
+    // keeps pending DMAs apart from reads of another stage except where it
+    // merges the two ways into the loop head (there it drains), so the loop
+    // body holds kSteps steps: at K = 3072 one pass, no drain.
+    constexpr int kSteps = 12;
+    static_assert(kSteps % 3 == 0, "stages rotate with the step");
+    for (int s0 = 0; s0 < KT + 2; s0 += kSteps) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int st = s0 + u;
+            if (st >= KT + 2) break;
+            uint8_t *in = u % 3 == 0 ? gemm_st0 : u % 3 == 1 ? gemm_st1 : gemm_st2;
+            const uint8_t *rd = u % 3 == 2 ? gemm_st0 : u % 3 == 0 ? gemm_st1 : gemm_st2;
+            KQ_WAIT_VM(kDPerTile);
+            __builtin_amdgcn_s_barrier();
+            issue(st < KT ? st : KT - 1, in);
+            if (st >= 2) compute(rd, st - 2);
+        }
+    }
+    // the repeats of the last tile may still be landing: drain, then the
+    // stages hold the output tile (rows 0..63 in stage 0, 64..127 in stage 1)
+    KQ_WAIT_VM(0);
+    __syncthreads();
+
+    // ---- epilogue: as in w4a4_gemm_kernel ----
+    static_assert(kBM == 128 && 64 * kBN * 2 <= kDStage, "two halves of the output tile");
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = wm * 64 + j * 32 + i32;
+        uint8_t *ob = wm == 0 ? gemm_st0 : gemm_st1;
+        const int lr = row & 63;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s8 = wn * 16 + i * 8 + 2 * q + kg;
+                const uint32_t lo = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
+                const uint32_t hi = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
+                *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int kRowChunks = kBN * 2 / 16;
+#pragma unroll
+    for (int k = 0; k < kBM * kRowChunks / kGemmThreads; ++k) {
+        const int f = tid + k * kGemmThreads;
+        const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
+        const uint8_t *ob = row < 64 ? gemm_st0 : gemm_st1;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(ob + (row & 63) * (kBN * 2) + 16 * (ch ^ (g >> 1)));
+        if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int gr = m0 + row, col = n0 + 8 * ch;
+        if (gr >= M || col >= N) continue;
+        uint16_t *yp = y + (int64_t)gr * ldy + col;
+        if (col + 7 < N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t *wc,
                              const uint8_t *ws, uint16_t *y, int M, int N, int K, int64_t ldy,
                              void *stream) {
@@ -255,15 +487,22 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     if (grid > INT32_MAX) return KQ_ERR_SHAPE;
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
-    const void *fn = (const void *)w4a4_gemm_kernel;
+    static int dma = -1;
+    if (dma < 0) {
+        const char *e = getenv("KQ_GEMM_DMA");
+        dma = e ? (atoi(e) != 0) : 1;
+    }
+    const void *fn = dma ? (const void *)w4a4_gemm_dma_kernel : (const void *)w4a4_gemm_kernel;
+    const size_t dyn = dma ? 0 : kGemmLds;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds) != hipSuccess)
+        if (hipFuncSetAttribute((const void *)w4a4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmLds) != hipSuccess)
             return KQ_ERR_HIP;
         attr_set = true;
     }
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args,
-                                         kGemmLds, (hipStream_t)stream);
+                                         dyn, (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
