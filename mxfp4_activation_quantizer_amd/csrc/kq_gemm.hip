@@ -17,21 +17,38 @@
 //
 // Tiling: 8 waves (2 along M x 4 along N) compute a 128 x 256 tile of Y, each
 // wave 64 x 64 (2 x 2 MFMA tiles).  K advances in tiles of 256 (four MFMA
-// steps; 128 code bytes and 8 scale bytes per row) through double-buffered
-// LDS: the next tile's global loads are issued before the current tile's
-// MFMAs and written to the other buffer after them.  With one workgroup per
-// CU the wait for those loads is the cost of an iteration, so the K tile is
-// as long as the LDS allows.  All loads are unconditional (clamped indices),
-// so the compiler's memory waits count exactly.  In LDS a code row is eight
-// 16-byte chunks stored at slot c ^ ((row >> 1) & 7): the 16 lanes that one
-// LDS cycle serves read 16 consecutive rows at the same chunk and hit 16
-// distinct slots of a 256-byte bank window.
+// steps; 128 code bytes and 8 scale bytes per row).  The operand tiles go
+// from global memory straight into LDS (global_load_lds_dwordx4 for codes,
+// _dword for scales) through three LDS stages: two K tiles are in flight
+// while a third is multiplied, and no registers hold them on the way.
+// In LDS a code row is eight 16-byte chunks stored at slot
+// c ^ ((row >> 1) & 7): the 16 lanes that one LDS cycle serves read 16
+// consecutive rows at the same chunk and hit 16 distinct slots of a
+// 256-byte bank window.  A DMA lane writes 16 bytes at (region base +
+// 16 * lane), so that layout is made on the global side: the lane that
+// lands in slot s of a row fetches chunk s ^ ((row >> 1) & 7).  A row's 8
+// scale bytes are read as one 8-byte word per tile (byte reads conflict on
+// gfx950) and the MFMA's scale operand select picks the byte of each step.
+//
+// Waits are explicit: before tile kt is read, vmcnt(one tile's DMAs)
+// retires tile kt's DMAs and leaves tile kt + 1's in flight; the barrier
+// after it also tells every wave that the stage of tile kt - 1 is free, and
+// the DMAs of tile kt + 2 go into that stage.  The stages are three separate
+// LDS arrays, so the compiler sees that the pending DMAs (into the other
+// two) do not alias the reads and adds no waits of its own, except where it
+// merges the two ways into a loop head; the loop body therefore holds 15
+// steps (one pass for K up to 3328).
 //
 // Workgroup order: XCD x (workgroups go to the 8 XCDs round-robin) takes a
 // contiguous range of an order that walks four M tiles for each N tile, so
 // each W tile is fetched into that XCD's L2 once for four workgroups.
-// A K that is a multiple of 128 but not of 256 ends with a half tile whose
-// upper half is zero codes with zero scale bytes (exact zeros in the sum).
+// A K that is a multiple of 128 but not of 256 ends with a half tile: its
+// missing half re-reads the valid half (never used) and only its first two
+// MFMA steps run.
+//
+// Epilogue: the bf16 tile is written into two of the (then free) stages, in
+// an XOR slot layout that keeps the 32-row accumulator stores conflict-free,
+// and every wave stores two whole 512-byte tile rows per instruction.
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -52,215 +69,11 @@ constexpr int kBM = 64 * kGemmWM, kBN = 64 * kGemmWN;
 constexpr int kGemmThreads = 64 * kGemmWM * kGemmWN;
 constexpr int kBK = 256;                          // K elements per LDS tile
 constexpr int kRowBytes = kBK / 2;                // 128 code bytes per row per tile
-constexpr int kChunks = kRowBytes / 16;           // 8 chunks of 16 bytes
 constexpr int kMGroup = 4;                        // M tiles that share a W tile
 constexpr int kAB = kBM * kRowBytes, kWB = kBN * kRowBytes;
-constexpr int kScaleSlots = (kBM + kBN + kGemmThreads - 1) / kGemmThreads * kGemmThreads;
-constexpr int kStage = kAB + kWB + 8 * kScaleSlots;  // codes + 8 scale bytes per row slot
-constexpr int kGemmLds = 2 * kStage;
-constexpr int kAPer = kBM * kChunks / kGemmThreads, kWPer = kBN * kChunks / kGemmThreads;
-constexpr int kSPer = kScaleSlots / kGemmThreads;
-static_assert(kBM * kChunks % kGemmThreads == 0 && kBN * kChunks % kGemmThreads == 0, "split");
 
 __device__ __forceinline__ int swz_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
-    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
-    const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldy, int mtc, int ntc) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-
-    // ---- workgroup -> (M tile, N tile) ----
-    const int tiles = mtc * ntc, per = (tiles + 7) / 8;
-    const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (lin >= tiles) return;
-    const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
-    const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
-    const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
-    const int m0 = mt * kBM, n0 = nt * kBN;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / kGemmWN, wn = wave % kGemmWN;
-    const int i32 = lane & 31, kg = lane >> 5;
-    const int K2 = K / 2, K32 = K / 32;
-    const int KT = (K + kBK - 1) / kBK;       // the last tile may be a half tile
-    const bool half_tail = (K % kBK) != 0;
-
-    // ---- per-thread load plan: byte offsets (rows clamped) and LDS slots ----
-    int ga[kAPer], gw[kWPer], la[kAPer], lw[kWPer], cha[kAPer], chw[kWPer];
-#pragma unroll
-    for (int q = 0; q < kAPer; ++q) {
-        const int c = tid + q * kGemmThreads, row = c / kChunks, ch = c % kChunks;
-        const int gr = m0 + row < M ? m0 + row : M - 1;
-        ga[q] = gr * K2 + 16 * ch;
-        la[q] = row * kRowBytes + 16 * swz_slot(row, ch);
-        cha[q] = ch;
-    }
-#pragma unroll
-    for (int q = 0; q < kWPer; ++q) {
-        const int c = tid + q * kGemmThreads, row = c / kChunks, ch = c % kChunks;
-        const int gr = n0 + row < N ? n0 + row : N - 1;
-        gw[q] = gr * K2 + 16 * ch;
-        lw[q] = kAB + row * kRowBytes + 16 * swz_slot(row, ch);
-        chw[q] = ch;
-    }
-    // scale slots: A rows then W rows; slots past BM + BN repeat the last row
-    int gs[kSPer];
-    const uint8_t *sbase[kSPer];
-#pragma unroll
-    for (int q = 0; q < kSPer; ++q) {
-        int v = tid + q * kGemmThreads;
-        v = v < kBM + kBN ? v : kBM + kBN - 1;
-        const int ra = m0 + v < M ? m0 + v : M - 1;
-        const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
-        sbase[q] = v < kBM ? as : ws;
-        gs[q] = (v < kBM ? ra : rw) * K32;
-    }
-
-    struct Regs { u32x4 a[kAPer], w[kWPer]; u32x2g s[kSPer]; };
-    auto gload = [&](int kt, Regs &r) {
-        // in a half tile, chunks 4..7 and scale word 1 re-read the valid
-        // half and are zeroed below
-        const bool half = half_tail && kt == KT - 1;
-#pragma unroll
-        for (int q = 0; q < kSPer; ++q) {
-            const uint32_t *p = reinterpret_cast<const uint32_t *>(sbase[q] + gs[q] + kt * 8);
-            r.s[q] = u32x2g{p[0], p[half ? 0 : 1]};
-            if (half) r.s[q][1] = 0u;
-        }
-#pragma unroll
-        for (int q = 0; q < kAPer; ++q) {
-            const int back = half && cha[q] >= 4 ? 64 : 0;
-            r.a[q] = *reinterpret_cast<const u32x4 *>(ac + ga[q] + kt * kRowBytes - back);
-            if (back) r.a[q] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int q = 0; q < kWPer; ++q) {
-            const int back = half && chw[q] >= 4 ? 64 : 0;
-            r.w[q] = *reinterpret_cast<const u32x4 *>(wc + gw[q] + kt * kRowBytes - back);
-            if (back) r.w[q] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto lstore = [&](int buf, const Regs &r) {
-        uint8_t *b = lds + buf * kStage;
-#pragma unroll
-        for (int q = 0; q < kAPer; ++q) *reinterpret_cast<u32x4 *>(b + la[q]) = r.a[q];
-#pragma unroll
-        for (int q = 0; q < kWPer; ++q) *reinterpret_cast<u32x4 *>(b + lw[q]) = r.w[q];
-        u32x2g *s = reinterpret_cast<u32x2g *>(b + kAB + kWB);
-#pragma unroll
-        for (int q = 0; q < kSPer; ++q) s[tid + q * kGemmThreads] = r.s[q];
-    };
-
-    f32x16g acc[2][2];  // [n tile][m tile]
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
-
-    auto compute = [&](int buf) {
-        const uint8_t *b = lds + buf * kStage;
-        const uint8_t *s = b + kAB + kWB;  // 8 scale bytes per row slot
-#pragma unroll
-        for (int ks = 0; ks < kBK / 64; ++ks) {
-            const int ch = 2 * ks + kg;  // this lane's 16-byte chunk of the row
-            i32x8 fa[2];
-            int sa[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int row = wm * 64 + j * 32 + i32;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(b + row * kRowBytes + 16 * swz_slot(row, ch));
-                fa[j] = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
-                sa[j] = s[row * 8 + ch];
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = wn * 64 + i * 32 + i32;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(b + kAB + row * kRowBytes + 16 * swz_slot(row, ch));
-                const i32x8 fw = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
-                const int sw = s[(kBM + row) * 8 + ch];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fa[j], acc[i][j], 4, 4,
-                                                                                0, sw, 0, sa[j]);
-            }
-        }
-    };
-
-    Regs r;
-    gload(0, r);
-    lstore(0, r);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) gload(kt + 1, r);
-        compute(kt & 1);
-        if (kt + 1 < KT) lstore((kt + 1) & 1, r);
-        __syncthreads();
-    }
-
-    // ---- epilogue: bf16 (nearest even) through LDS, whole rows per store ----
-    // Written straight from the accumulators, each store instruction would
-    // put 16 bytes into each of 32 rows (a line completed over eight
-    // instructions), which halves HBM write throughput.  The tile goes to
-    // LDS first (free after the loop's last barrier): element (r, c) sits in
-    // 8-byte slot (c / 4) ^ (r & 31) of a 512-byte row, so the 32 rows one
-    // accumulator store touches hit 32 distinct slots of a bank window.
-    // Then each thread stores 16 bytes = 8 columns of one row: a wave writes
-    // two whole 512-byte tile rows per instruction.
-    static_assert(kBM * kBN * 2 <= kGemmLds, "the output tile fits the LDS");
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = wm * 64 + j * 32 + i32;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s8 = wn * 16 + i * 8 + 2 * q + kg;  // (column / 4) in the tile
-                const uint32_t lo = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
-                const uint32_t hi = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
-                *reinterpret_cast<u32x2g *>(lds + row * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
-            }
-        }
-    }
-    __syncthreads();
-    constexpr int kRowChunks = kBN * 2 / 16;  // 16-byte chunks per tile row
-#pragma unroll
-    for (int k = 0; k < kBM * kRowChunks / kGemmThreads; ++k) {
-        const int f = tid + k * kGemmThreads;
-        const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
-        u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * (kBN * 2) + 16 * (ch ^ (g >> 1)));
-        if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int gr = m0 + row, col = n0 + 8 * ch;
-        if (gr >= M || col >= N) continue;
-        uint16_t *yp = y + (int64_t)gr * ldy + col;
-        if (col + 7 < N) {
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS form: the same tiles, waves, MFMAs and epilogue, but the
-// operand tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4 for codes, _dword for scales) through three LDS
-// stages, so two K tiles are in flight while a third is multiplied and no
-// registers hold them on the way.  A DMA lane writes 16 bytes at (stage
-// base + 16 * lane), so the XOR slot layout is made on the global side: the
-// lane that lands in slot s of a row fetches chunk s ^ ((row >> 1) & 7).
-// Waits are explicit: before tile kt is read, vmcnt(one tile's DMAs) retires
-// tile kt's DMAs and leaves tile kt + 1's in flight; the barrier after it
-// also tells every wave that the stage of tile kt - 1 is free, and the DMAs
-// of tile kt + 2 go into that stage.  The stages are three separate LDS
-// arrays, so the compiler sees that the pending DMAs (into the other two)
-// do not alias the reads and adds no waits of its own.
-// ---------------------------------------------------------------------------
 constexpr int kDScale = 8 * (kBM + kBN);         // 8 scale bytes per A and W row
 constexpr int kDStage = kAB + kWB + kDScale;     // 52224 bytes
 constexpr int kDA = kAB / 1024 / (kGemmThreads / 64);     // A DMAs (1 KB per wave) per wave
@@ -313,42 +126,67 @@ __device__ __forceinline__ void gemm_issue(const DmaPlan &pl, const uint8_t *ac,
         dma4(pl.sb[q] + pl.gs[q] + kt * 8 - (half && pl.his[q] ? 4 : 0), st + kAB + kWB + pl.rs[q] * 256);
 }
 
-// nks K steps of 64 from stage b into the wave's 2 x 2 accumulator tiles.
-__device__ __forceinline__ void gemm_compute(const uint8_t *__restrict__ b, int nks, int wm, int wn,
-                                             int i32, int kg, f32x16g (&acc)[2][2]) {
-    const uint8_t *sc = b + kAB + kWB;
+// One K step of 64: the lane's A and W fragments (chunk 2 KS + kg of its
+// rows) and the scale bytes, which sit at byte 2 KS of each row's scale
+// word pair (see gemm_compute); the MFMA's scale operand select (0..3)
+// takes the byte, so no shifts per step.
+template <int KS>
+__device__ __forceinline__ void gemm_kstep(const uint8_t *__restrict__ b, int wm, int wn, int i32, int kg,
+                                           const u32x2g (&sa)[2], const u32x2g (&sw)[2],
+                                           f32x16g (&acc)[2][2]) {
+    constexpr int kSel = 2 * (KS & 1), kWord = KS >> 1;
+    const int ch = 2 * KS + kg;
+    i32x8 fa[2];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 64; ++ks) {
-        if (ks >= nks) break;
-        const int ch = 2 * ks + kg;
-        i32x8 fa[2];
-        int sa[2];
+    for (int j = 0; j < 2; ++j) {
+        const int row = wm * 64 + j * 32 + i32;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(b + row * kRowBytes + 16 * swz_slot(row, ch));
+        fa[j] = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+    }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = wm * 64 + j * 32 + i32;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(b + row * kRowBytes + 16 * swz_slot(row, ch));
-            fa[j] = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
-            sa[j] = sc[row * 8 + ch];
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int row = wn * 64 + i * 32 + i32;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(b + kAB + row * kRowBytes + 16 * swz_slot(row, ch));
+        const i32x8 fw = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = wn * 64 + i * 32 + i32;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(b + kAB + row * kRowBytes + 16 * swz_slot(row, ch));
-            const i32x8 fw = (i32x8)__builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
-            const int sw = sc[(kBM + row) * 8 + ch];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fa[j], acc[i][j], 4, 4, 0,
-                                                                            sw, 0, sa[j]);
-        }
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fw, fa[j], acc[i][j], 4, 4, kSel, (int)sw[i][kWord], kSel, (int)sa[j][kWord]);
     }
 }
 
-__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_dma_kernel(
+// nks K steps of 64 from stage b into the wave's 2 x 2 accumulator tiles.
+// Scales: one 8-byte read per row per tile (byte reads conflict on gfx950:
+// two extra cycles each), shifted right one byte for the lanes of the upper
+// 32 K values (kg = 1), so that K step ks finds its byte at 2 ks for every
+// lane.
+__device__ __forceinline__ void gemm_compute(const uint8_t *__restrict__ b, int nks, int wm, int wn,
+                                             int i32, int kg, f32x16g (&acc)[2][2]) {
+    const uint8_t *sc = b + kAB + kWB;
+    u32x2g sa[2], sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + (wm * 64 + j * 32 + i32) * 8) >> (8 * kg);
+        sa[j] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + (kBM + wn * 64 + i * 32 + i32) * 8) >> (8 * kg);
+        sw[i] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+    }
+    gemm_kstep<0>(b, wm, wn, i32, kg, sa, sw, acc);
+    gemm_kstep<1>(b, wm, wn, i32, kg, sa, sw, acc);
+    if (nks > 2) {
+        gemm_kstep<2>(b, wm, wn, i32, kg, sa, sw, acc);
+        gemm_kstep<3>(b, wm, wn, i32, kg, sa, sw, acc);
+    }
+}
+
+__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldy, int mtc, int ntc) {
-    // ---- workgroup -> (M tile, N tile), as in w4a4_gemm_kernel ----
+    // ---- workgroup -> (M tile, N tile) ----
     const int tiles = mtc * ntc, per = (tiles + 7) / 8;
     const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (lin >= tiles) return;
@@ -415,8 +253,9 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_dma_kernel(
     // tile issue a repeat of it (never read).  The compiler's wait insertion
     // keeps pending DMAs apart from reads of another stage except where it
     // merges the two ways into the loop head (there it drains), so the loop
-    // body holds kSteps steps: at K = 3072 one pass, no drain.
-    constexpr int kSteps = 12;
+    // body holds kSteps steps: K up to 3328 (13 tiles, 15 steps) takes one
+    // pass with no drain.
+    constexpr int kSteps = 15;
     static_assert(kSteps % 3 == 0, "stages rotate with the step");
     for (int s0 = 0; s0 < KT + 2; s0 += kSteps) {
 #pragma unroll
@@ -436,7 +275,7 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_dma_kernel(
     KQ_WAIT_VM(0);
     __syncthreads();
 
-    // ---- epilogue: as in w4a4_gemm_kernel ----
+    // ---- epilogue: bf16 (nearest even) through LDS, whole rows per store ----
     static_assert(kBM == 128 && 64 * kBN * 2 <= kDStage, "two halves of the output tile");
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -487,22 +326,9 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     if (grid > INT32_MAX) return KQ_ERR_SHAPE;
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
-    static int dma = -1;
-    if (dma < 0) {
-        const char *e = getenv("KQ_GEMM_DMA");
-        dma = e ? (atoi(e) != 0) : 1;
-    }
-    const void *fn = dma ? (const void *)w4a4_gemm_dma_kernel : (const void *)w4a4_gemm_kernel;
-    const size_t dyn = dma ? 0 : kGemmLds;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)w4a4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kGemmLds) != hipSuccess)
-            return KQ_ERR_HIP;
-        attr_set = true;
-    }
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args,
-                                         dyn, (hipStream_t)stream);
+    const void *fn = (const void *)w4a4_gemm_kernel;
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
