@@ -186,134 +186,142 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldy, int mtc, int ntc) {
-    // ---- workgroup -> (M tile, N tile) ----
-    const int tiles = mtc * ntc, per = (tiles + 7) / 8;
-    const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (lin >= tiles) return;
-    const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
-    const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
-    const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
-    const int m0 = mt * kBM, n0 = nt * kBN;
+    // ---- persistent: workgroup w of XCD x (workgroups go to the XCDs
+    //      round-robin) takes tiles w, w + wpx, ... of that XCD's contiguous
+    //      range of an order that walks four M tiles for each N tile; its
+    //      output stores drain while the next tile's first DMAs are in flight
+    const int tiles = mtc * ntc, per = (tiles + 7) / 8, wpx = gridDim.x >> 3;
+    for (int t = blockIdx.x >> 3; t < per; t += wpx) {
+        const int lin = (blockIdx.x & 7) * per + t;
+        if (lin >= tiles) break;
+        const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
+        const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
+        const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
+        const int m0 = mt * kBM, n0 = nt * kBN;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / kGemmWN, wn = wave % kGemmWN;
-    const int i32 = lane & 31, kg = lane >> 5;
-    const int K2 = K / 2, K32 = K / 32;
-    const int KT = (K + kBK - 1) / kBK;
-    const bool half_tail = (K % kBK) != 0;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / kGemmWN, wn = wave % kGemmWN;
+        const int i32 = lane & 31, kg = lane >> 5;
+        const int K2 = K / 2, K32 = K / 32;
+        const int KT = (K + kBK - 1) / kBK;
+        const bool half_tail = (K % kBK) != 0;
 
-    // ---- DMA plan: source offsets of this lane, one region per DMA ----
-    DmaPlan pl;
+        // ---- DMA plan: source offsets of this lane, one region per DMA ----
+        DmaPlan pl;
 #pragma unroll
-    for (int q = 0; q < kDA; ++q) {
-        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the A tile
-        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-        pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
-        pl.hia[q] = c >= 4;
-    }
-#pragma unroll
-    for (int q = 0; q < kDW; ++q) {
-        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
-        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-        pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
-        pl.hiw[q] = c >= 4;
-    }
-#pragma unroll
-    for (int q = 0; q < kDS; ++q) {
-        int r = q * (kGemmThreads / 64) + wave;
-        r = r < kDSRegions ? r : r - (kGemmThreads / 64);  // past the last: a repeat
-        pl.rs[q] = r;
-        const int dw = r * 64 + lane, v = dw >> 1, hf = dw & 1;  // row slot, dword of its 8 bytes
-        const int ra = m0 + v < M ? m0 + v : M - 1;
-        const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
-        pl.sb[q] = v < kBM ? as : ws;
-        pl.gs[q] = (v < kBM ? ra : rw) * K32 + 4 * hf;
-        pl.his[q] = hf;
-    }
-
-    auto issue = [&](int kt, uint8_t *st) {
-        gemm_issue(pl, ac, wc, kt, half_tail && kt == KT - 1, wave, st);
-    };
-
-    f32x16g acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
-
-    auto compute = [&](const uint8_t *b, int kt) {
-        gemm_compute(b, half_tail && kt == KT - 1 ? 2 : kBK / 64, wm, wn, i32, kg, acc);
-    };
-
-    // ---- three stages: step s issues tile s and multiplies tile s - 2 ----
-    // Step s: vmcnt(one tile) retires tile s - 2 (tile s - 1 stays in
-    // flight); the barrier makes every wave's DMAs of tile s - 2 visible and
-    // frees the stage of tile s - 3, which takes tile s.  Steps past the last
-    // tile issue a repeat of it (never read).  The compiler's wait insertion
-    // keeps pending DMAs apart from reads of another stage except where it
-    // merges the two ways into the loop head (there it drains), so the loop
-    // body holds kSteps steps: K up to 3328 (13 tiles, 15 steps) takes one
-    // pass with no drain.
-    constexpr int kSteps = 15;
-    static_assert(kSteps % 3 == 0, "stages rotate with the step");
-    for (int s0 = 0; s0 < KT + 2; s0 += kSteps) {
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const int st = s0 + u;
-            if (st >= KT + 2) break;
-            uint8_t *in = u % 3 == 0 ? gemm_st0 : u % 3 == 1 ? gemm_st1 : gemm_st2;
-            const uint8_t *rd = u % 3 == 2 ? gemm_st0 : u % 3 == 0 ? gemm_st1 : gemm_st2;
-            KQ_WAIT_VM(kDPerTile);
-            __builtin_amdgcn_s_barrier();
-            issue(st < KT ? st : KT - 1, in);
-            if (st >= 2) compute(rd, st - 2);
+        for (int q = 0; q < kDA; ++q) {
+            const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the A tile
+            const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+            pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
+            pl.hia[q] = c >= 4;
         }
-    }
-    // the repeats of the last tile may still be landing: drain, then the
-    // stages hold the output tile (rows 0..63 in stage 0, 64..127 in stage 1)
-    KQ_WAIT_VM(0);
-    __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kDW; ++q) {
+            const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
+            const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+            pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
+            pl.hiw[q] = c >= 4;
+        }
+#pragma unroll
+        for (int q = 0; q < kDS; ++q) {
+            int r = q * (kGemmThreads / 64) + wave;
+            r = r < kDSRegions ? r : r - (kGemmThreads / 64);  // past the last: a repeat
+            pl.rs[q] = r;
+            const int dw = r * 64 + lane, v = dw >> 1, hf = dw & 1;  // row slot, dword of its 8 bytes
+            const int ra = m0 + v < M ? m0 + v : M - 1;
+            const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
+            pl.sb[q] = v < kBM ? as : ws;
+            pl.gs[q] = (v < kBM ? ra : rw) * K32 + 4 * hf;
+            pl.his[q] = hf;
+        }
 
-    // ---- epilogue: bf16 (nearest even) through LDS, whole rows per store ----
-    static_assert(kBM == 128 && 64 * kBN * 2 <= kDStage, "two halves of the output tile");
+        auto issue = [&](int kt, uint8_t *st) {
+            gemm_issue(pl, ac, wc, kt, half_tail && kt == KT - 1, wave, st);
+        };
+
+        f32x16g acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = wm * 64 + j * 32 + i32;
-        uint8_t *ob = wm == 0 ? gemm_st0 : gemm_st1;
-        const int lr = row & 63;
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
+
+        auto compute = [&](const uint8_t *b, int kt) {
+            gemm_compute(b, half_tail && kt == KT - 1 ? 2 : kBK / 64, wm, wn, i32, kg, acc);
+        };
+
+        // ---- three stages: step s issues tile s and multiplies tile s - 2 ----
+        // Step s: vmcnt(one tile) retires tile s - 2 (tile s - 1 stays in
+        // flight); the barrier makes every wave's DMAs of tile s - 2 visible and
+        // frees the stage of tile s - 3, which takes tile s.  Steps past the last
+        // tile issue a repeat of it (never read).  The compiler's wait insertion
+        // keeps pending DMAs apart from reads of another stage except where it
+        // merges the two ways into the loop head (there it drains), so the loop
+        // body holds kSteps steps: K up to 3328 (13 tiles, 15 steps) takes one
+        // pass with no drain.
+        constexpr int kSteps = 15;
+        static_assert(kSteps % 3 == 0, "stages rotate with the step");
+        for (int s0 = 0; s0 < KT + 2; s0 += kSteps) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s8 = wn * 16 + i * 8 + 2 * q + kg;
-                const uint32_t lo = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
-                const uint32_t hi = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
-                *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
+            for (int u = 0; u < kSteps; ++u) {
+                const int st = s0 + u;
+                if (st >= KT + 2) break;
+                uint8_t *in = u % 3 == 0 ? gemm_st0 : u % 3 == 1 ? gemm_st1 : gemm_st2;
+                const uint8_t *rd = u % 3 == 2 ? gemm_st0 : u % 3 == 0 ? gemm_st1 : gemm_st2;
+                KQ_WAIT_VM(kDPerTile);
+                __builtin_amdgcn_s_barrier();
+                issue(st < KT ? st : KT - 1, in);
+                if (st >= 2) compute(rd, st - 2);
             }
         }
-    }
-    __syncthreads();
-    constexpr int kRowChunks = kBN * 2 / 16;
+        // the repeats of the last tile may still be landing: drain, then the
+        // stages hold the output tile (rows 0..63 in stage 0, 64..127 in stage 1)
+        KQ_WAIT_VM(0);
+        __syncthreads();
+
+        // ---- epilogue: bf16 (nearest even) through LDS, whole rows per store ----
+        static_assert(kBM == 128 && 64 * kBN * 2 <= kDStage, "two halves of the output tile");
 #pragma unroll
-    for (int k = 0; k < kBM * kRowChunks / kGemmThreads; ++k) {
-        const int f = tid + k * kGemmThreads;
-        const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
-        const uint8_t *ob = row < 64 ? gemm_st0 : gemm_st1;
-        u32x4 v = *reinterpret_cast<const u32x4 *>(ob + (row & 63) * (kBN * 2) + 16 * (ch ^ (g >> 1)));
-        if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int gr = m0 + row, col = n0 + 8 * ch;
-        if (gr >= M || col >= N) continue;
-        uint16_t *yp = y + (int64_t)gr * ldy + col;
-        if (col + 7 < N) {
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
-        } else {
+        for (int j = 0; j < 2; ++j) {
+            const int row = wm * 64 + j * 32 + i32;
+            uint8_t *ob = wm == 0 ? gemm_st0 : gemm_st1;
+            const int lr = row & 63;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int s8 = wn * 16 + i * 8 + 2 * q + kg;
+                    const uint32_t lo = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
+                    const uint32_t hi = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
+                    *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
+                }
+            }
         }
+        __syncthreads();
+        constexpr int kRowChunks = kBN * 2 / 16;
+#pragma unroll
+        for (int k = 0; k < kBM * kRowChunks / kGemmThreads; ++k) {
+            const int f = tid + k * kGemmThreads;
+            const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
+            const uint8_t *ob = row < 64 ? gemm_st0 : gemm_st1;
+            u32x4 v = *reinterpret_cast<const u32x4 *>(ob + (row & 63) * (kBN * 2) + 16 * (ch ^ (g >> 1)));
+            if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+            const int gr = m0 + row, col = n0 + 8 * ch;
+            if (gr >= M || col >= N) continue;
+            uint16_t *yp = y + (int64_t)gr * ldy + col;
+            if (col + 7 < N) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        // every wave is done reading the staged output before the next
+        // tile's DMAs land in those stages
+        __syncthreads();
     }
 }
 
@@ -322,8 +330,25 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
                              void *stream) {
     const int mtc = (M + kBM - 1) / kBM, ntc = (N + kBN - 1) / kBN;
     const int64_t tiles = (int64_t)mtc * ntc;
-    const int64_t grid = (tiles + 7) / 8 * 8;
-    if (grid > INT32_MAX) return KQ_ERR_SHAPE;
+    if (tiles > INT32_MAX) return KQ_ERR_SHAPE;
+    // one workgroup per CU (the LDS holds one), a multiple of the 8 XCDs;
+    // KQ_GEMM_WPX (read once) overrides the workgroups per XCD
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+    static int c_dev = -1, c_wpx = 0;
+    if (dev != c_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return KQ_ERR_HIP;
+        c_wpx = cus / 8 > 0 ? cus / 8 : 1;
+        if (const char *e = getenv("KQ_GEMM_WPX")) {
+            const int v = atoi(e);
+            if (v > 0) c_wpx = v;
+        }
+        c_dev = dev;
+    }
+    const int64_t per = (tiles + 7) / 8;
+    const int64_t grid = 8 * (per < c_wpx ? per : c_wpx);
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
     const void *fn = (const void *)w4a4_gemm_kernel;
