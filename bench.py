@@ -40,7 +40,7 @@ CSRC = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
 
 # The files the quantizer kernel is built from: a counter summary stays valid
 # until one of them changes.
-QUANT_SOURCES = ("kq_quant.hip", "kq_kron.h", "kq_device.h", "Makefile")
+QUANT_SOURCES = ("kq_quant.hip", "kq_kron.h", "kq_device.h", "kq_host.h", "Makefile")
 
 
 def kernel_source_hash() -> str:

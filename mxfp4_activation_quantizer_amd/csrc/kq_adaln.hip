@@ -33,6 +33,7 @@
 
 #include "kq.h"
 #include "kq_device.h"
+#include "kq_host.h"
 #include "kq_kron.h"
 
 namespace kq {
@@ -243,29 +244,17 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
 // about 384 threads measured fastest (17.0 us against 20.0 and 25.5 us).
 // KQ_ADALN_ROWS_PER_THREAD (1, 2 or 4; read once) overrides it for sweeps.
 static int adaln_rows_per_thread() {
-    static int cached = 0;
-    if (cached == 0) {
-        int v = 1;
-        const char *e = getenv("KQ_ADALN_ROWS_PER_THREAD");
-        if (e) {
-            const int q = atoi(e);
-            if (q == 1 || q == 2 || q == 4) v = q;
-        }
-        cached = v;
-    }
-    return cached;
+    static const int v = env_override("KQ_ADALN_ROWS_PER_THREAD", 1,
+                                      [](int q) { return q == 1 || q == 2 || q == 4; });
+    return v;
 }
 
 // Row groups per workgroup: among G with G * nb <= 512 threads, the one whose
 // G * nb threads fill whole waves best; ties go to the G whose workgroup is
 // closest to KQ_ADALN_THREADS threads (default 384, read once; for sweeps).
 static int adaln_groups(int nb) {
-    static int target = 0;
-    if (target == 0) {
-        const char *e = getenv("KQ_ADALN_THREADS");
-        const int v = e ? atoi(e) : 0;
-        target = v >= 64 && v <= 512 ? v : 384;
-    }
+    static const int target =
+        env_override("KQ_ADALN_THREADS", 384, [](int v) { return v >= 64 && v <= 512; });
     int best = 1;
     double best_util = -1.0;
     int best_dist = 1 << 30;
@@ -293,12 +282,14 @@ static kq_status launch_adaln(AdalnArgs a, void *stream) {
     a.wps = (int)wps;
     const size_t lds = sizeof(float) * (2 * (size_t)a.d + 2 * (size_t)ROWS * a.nb);
     auto kern = adaln_kernel<U, QUANT>;
-    static bool attr_set = false;
-    if (!attr_set) {
+    static DeviceOnce attr_set;  // the attribute is per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+    if (!attr_set.done(dev)) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 96 * 1024) != hipSuccess)
             return KQ_ERR_HIP;
-        attr_set = true;
+        attr_set.set(dev);
     }
     void *argv[] = {(void *)&a};
     const hipError_t e = hipLaunchKernel((const void *)kern, dim3((unsigned)(samples * wps)),

@@ -57,6 +57,7 @@
 
 #include "kq.h"
 #include "kq_device.h"
+#include "kq_host.h"
 
 namespace kq {
 
@@ -333,22 +334,20 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     if (tiles > INT32_MAX) return KQ_ERR_SHAPE;
     // one workgroup per CU (the LDS holds one), a multiple of the 8 XCDs;
     // KQ_GEMM_WPX (read once) overrides the workgroups per XCD
+    static const int wpx_env = env_override("KQ_GEMM_WPX", 0, [](int v) { return v > 0; });
+    static std::atomic<int> wpx_dev[64];  // per device; 0 = not yet known
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
-    static int c_dev = -1, c_wpx = 0;
-    if (dev != c_dev) {
+    int wpx = dev >= 0 && dev < 64 ? wpx_dev[dev].load(std::memory_order_relaxed) : 0;
+    if (wpx == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return KQ_ERR_HIP;
-        c_wpx = cus / 8 > 0 ? cus / 8 : 1;
-        if (const char *e = getenv("KQ_GEMM_WPX")) {
-            const int v = atoi(e);
-            if (v > 0) c_wpx = v;
-        }
-        c_dev = dev;
+        wpx = wpx_env > 0 ? wpx_env : (cus / 8 > 0 ? cus / 8 : 1);
+        if (dev >= 0 && dev < 64) wpx_dev[dev].store(wpx, std::memory_order_relaxed);
     }
     const int64_t per = (tiles + 7) / 8;
-    const int64_t grid = 8 * (per < c_wpx ? per : c_wpx);
+    const int64_t grid = 8 * (per < wpx ? per : wpx);
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
     const void *fn = (const void *)w4a4_gemm_kernel;

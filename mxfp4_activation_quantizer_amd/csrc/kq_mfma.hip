@@ -33,6 +33,7 @@
 
 #include "kq.h"
 #include "kq_device.h"
+#include "kq_host.h"
 
 namespace kq {
 
@@ -200,17 +201,9 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
 }
 
 static int mfma_tiles_per_wave() {
-    static int cached = 0;
-    if (cached == 0) {
-        int v = 2;
-        const char *e = getenv("KQ_MFMA_TILES_PER_WAVE");
-        if (e) {
-            int q = atoi(e);
-            if (q == 1 || q == 2 || q == 4 || q == 8) v = q;
-        }
-        cached = v;
-    }
-    return cached;
+    static const int v = env_override("KQ_MFMA_TILES_PER_WAVE", 2,
+                                      [](int q) { return q == 1 || q == 2 || q == 4 || q == 8; });
+    return v;
 }
 
 }  // namespace kq

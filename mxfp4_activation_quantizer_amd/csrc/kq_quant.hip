@@ -23,6 +23,7 @@
 
 #include "kq.h"
 #include "kq_device.h"
+#include "kq_host.h"
 #include "kq_kron.h"
 
 namespace kq {
@@ -345,17 +346,9 @@ struct Plan {
 // 3-8 % faster than 2, 4 or 8 units per lane on 4608 x 3072.
 // KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
 static int units_per_lane() {
-    static int cached = 0;
-    if (cached == 0) {
-        int v = 1;
-        const char *e = getenv("KQ_UNITS_PER_LANE");
-        if (e) {
-            int p = atoi(e);
-            if (p == 1 || p == 2 || p == 4 || p == 8) v = p;
-        }
-        cached = v;
-    }
-    return cached;
+    static const int v = env_override("KQ_UNITS_PER_LANE", 1,
+                                      [](int p) { return p == 1 || p == 2 || p == 4 || p == 8; });
+    return v;
 }
 
 static bool plan_launch(int64_t tokens, int nb, Plan &pl) {
