@@ -28,8 +28,8 @@
  *    in-block channel index, and y = x * T_j (row vector, as X*H in LRQ-DiT
  *    Sec. 3.2 Eq. (2)).  The Hadamard start of the summary's "Approach" is
  *    (l,u,v) = (1, 1/sqrt2, -1/sqrt2) for every factor.
- *  - MXFP4 output (the pages' "W4A4 MXFP4"; element and scale rules of the
- *    OCP MX v1.0 format):
+ *  - MXFP4 output (the pages' W4A4 MXFP4 setting; element and scale rules
+ *    of the OCP MX v1.0 format):
  *      codes  uint8 [tokens][d/2]: element k of a row in the low nibble of
  *             byte k/2 when k is even, in the high nibble when k is odd;
  *             each nibble is an E2M1 code (sign<<3 | magnitude index,
@@ -95,8 +95,8 @@ kq_status kq_transform_quant(const void *x, int64_t tokens, int64_t d, int64_t l
 /*
  * kq_transform_quant_mfma — the same quantizer with the block transform run
  * as a dense 32x32 product on the matrix cores, the formulation of the
- * KroQuant summary ("Approach": a single tensor-core GEMM per block) and
- * abstract ("small tensor-core GEMMs").  Same arguments, layouts and errors
+ * KroQuant summary (Approach: one matrix-core GEMM per block) and
+ * abstract (small matrix-core GEMMs).  Same arguments, layouts and errors
  * as kq_transform_quant.  T_j is materialised in fp32 and split into three
  * bf16 terms; the products accumulate in fp32 in the matrix core's own order,
  * so values agree with the exact y = x * T_j to within fp32 rounding (not
@@ -148,8 +148,8 @@ kq_status kq_mxfp4_quant_f32(const float *y, int64_t tokens, int64_t d, int64_t 
  * 32-channel block (along K) of every weight row is multiplied by T_j^-T and
  * the result is quantized to MXFP4 along K, so that
  * (X T)(W T^-T)^T = X W^T (LRQ-DiT Sec. 3.2 Eq. (2) with an invertible T;
- * KroQuant abstract: "its inverse to the weights").  Runs once per weight
- * matrix, offline.
+ * KroQuant abstract: the inverse transform goes to the weights).  Runs once
+ * per weight matrix, offline.
  *
  *   w       bf16 [rows = N][ld_w] (row-major, K = k contiguous), as for x
  *   lu      fp32 [k/32][5][3], the activation side's parameters
@@ -166,8 +166,8 @@ kq_status kq_weight_quant(const void *w, int64_t rows, int64_t k, int64_t ld_w,
  * kq_dequant_inverse — the inverse side: decode MXFP4 and undo the block
  * transform, x = dequant(codes, scales) * T_j^-1, rounded to bf16 (nearest
  * even).  The transform is invertible with unit determinant (KroQuant
- * summary, "Approach"; abstract: "applies an invertible linear transform to
- * the activations and its inverse to the weights").
+ * summary, "Approach"; abstract: the activations take the invertible
+ * transform and the weights its inverse).
  *
  *   codes   uint8 [tokens][d/2], 16-byte aligned (layout as above)
  *   scales  uint8 [tokens][d/32]
@@ -187,8 +187,8 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
  * kq_w4a4_gemm — the W4A4 consumer of the quantized activations:
  * Y = dequant(A) * dequant(W)^T with fp32 accumulation and bf16 output
  * (nearest even), on the gfx950 block-scaled matrix cores (E2M1 operands,
- * E8M0 scales).  The pages' setting is W4A4 MXFP4 (KroQuant summary; abstract
- * "W4A4 (MXFP4e2)"): A from kq_transform_quant, W from kq_weight_quant, so
+ * E8M0 scales).  The pages' setting is W4A4 MXFP4 (KroQuant summary and
+ * abstract): A from kq_transform_quant, W from kq_weight_quant, so
  * that Y approximates X * W_original^T (LRQ-DiT Sec. 3.2 Eq. (2)).
  *
  *   a_codes uint8 [M][K/2] (16-byte aligned), a_scales uint8 [M][K/32] (4-byte aligned)
