@@ -596,7 +596,10 @@ def _random_mxfp4(g, rows, k, lo=118, hi=128):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 128), (128, 256, 256), (100, 300, 384),
-                                   (1, 17, 128), (257, 129, 512)])
+                                   (1, 17, 128), (257, 129, 512),
+                                   # K past one 15-step pass of the K pipeline
+                                   # (3328), whole and ending in a half tile
+                                   (70, 260, 4096), (33, 40, 4224), (5, 8, 7808)])
 def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     torch = torch_cuda
     g = np.random.default_rng(M * 7 + N * 3 + K)
