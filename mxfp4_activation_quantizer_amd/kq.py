@@ -178,13 +178,55 @@ def _act(x, dtype_name: str):
     return x.shape[0], x.stride(0)
 
 
+_DTYPES = {"bf16": "bfloat16", "f32": "float32", "u8": "uint8"}
+
+
+def _dtype(name: str):
+    return getattr(_torch(), _DTYPES[name])
+
+
+def _param(t, name: str, device, dtype_name: str, numel: int):
+    """A tensor a kernel reads whole through a plain pointer: on ``device``,
+    of the dtype, contiguous, with at least ``numel`` elements.  Checked here
+    so that a host tensor or a short buffer never reaches a kernel."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != _dtype(dtype_name):
+        raise ValueError(f"{name} must be {_dtype(dtype_name)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {numel}")
+    return t
+
+
+def _rows_out(t, name: str, device, dtype_name: str, rows: int, cols: int):
+    """A 2-D output written row by row: [>= rows][>= cols] on ``device`` with
+    contiguous rows (the row stride is passed to the kernel)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != _dtype(dtype_name) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D {_dtype(dtype_name)} tensor")
+    if t.shape[0] < rows or t.shape[1] < cols or (rows > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be [>={rows}][>={cols}] with contiguous rows")
+    return t
+
+
 def _mxfp4_out(x, tokens: int, d: int, codes=None, scales=None):
     torch = _torch()
     if codes is None:
         codes = torch.empty((tokens, d // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((tokens, d // 32), dtype=torch.uint8, device=x.device)
+    _param(codes, "codes", x.device, "u8", tokens * (d // 2))
+    _param(scales, "scales", x.device, "u8", tokens * (d // 32))
     return codes, scales
+
+
+def _lu(lu, device, d: int):
+    return _param(lu, "lu", device, "f32", (d // 32) * 15)
 
 
 def transform_quant(x, lu, d: int | None = None, codes=None, scales=None):
@@ -192,6 +234,7 @@ def transform_quant(x, lu, d: int | None = None, codes=None, scales=None):
     tokens, ld = _act(x, "bf16")
     d = x.shape[1] if d is None else d
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _lu(lu, x.device, d)
     _check("kq_transform_quant", kq_transform_quant(
         x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
         _stream(x)))
@@ -203,6 +246,7 @@ def transform_quant_mfma(x, lu, d: int | None = None, codes=None, scales=None):
     tokens, ld = _act(x, "bf16")
     d = x.shape[1] if d is None else d
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _lu(lu, x.device, d)
     _check("kq_transform_quant_mfma", kq_transform_quant_mfma(
         x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
         _stream(x)))
@@ -215,6 +259,8 @@ def transform_f32(x, lu, d: int | None = None, y=None):
     d = x.shape[1] if d is None else d
     if y is None:
         y = torch.empty((tokens, d), dtype=torch.float32, device=x.device)
+    _param(y, "y", x.device, "f32", tokens * d)
+    _lu(lu, x.device, d)
     _check("kq_transform_f32", kq_transform_f32(
         x.data_ptr(), tokens, d, ld, lu.data_ptr(), y.data_ptr(), _stream(x)))
     return y
@@ -224,6 +270,7 @@ def smooth_quant(x, mult, d: int | None = None, codes=None, scales=None):
     tokens, ld = _act(x, "bf16")
     d = x.shape[1] if d is None else d
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _param(mult, "mult", x.device, "f32", d)
     _check("kq_smooth_quant", kq_smooth_quant(
         x.data_ptr(), tokens, d, ld, mult.data_ptr(), codes.data_ptr(), scales.data_ptr(),
         _stream(x)))
@@ -263,8 +310,12 @@ def dequant_inverse(codes, scales, lu, x_out=None):
     if codes.dtype != torch.uint8 or codes.dim() != 2 or not codes.is_cuda:
         raise ValueError("codes must be a 2-D uint8 GPU tensor")
     tokens, d = codes.shape[0], codes.shape[1] * 2
+    _param(codes, "codes", codes.device, "u8", tokens * (d // 2))
+    _param(scales, "scales", codes.device, "u8", tokens * (d // 32))
+    _lu(lu, codes.device, d)
     if x_out is None:
         x_out = torch.empty((tokens, d), dtype=torch.bfloat16, device=codes.device)
+    _rows_out(x_out, "x_out", codes.device, "bf16", tokens, d)
     _check("kq_dequant_inverse", kq_dequant_inverse(
         codes.data_ptr(), scales.data_ptr(), tokens, d, lu.data_ptr(), x_out.data_ptr(),
         x_out.stride(0), _stream(codes)))
@@ -276,6 +327,7 @@ def weight_quant(w, lu, k: int | None = None, codes=None, scales=None):
     rows, ld = _act(w, "bf16")
     k = w.shape[1] if k is None else k
     codes, scales = _mxfp4_out(w, rows, k, codes, scales)
+    _lu(lu, w.device, k)
     _check("kq_weight_quant", kq_weight_quant(
         w.data_ptr(), rows, k, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(), _stream(w)))
     return codes, scales
@@ -284,10 +336,18 @@ def weight_quant(w, lu, k: int | None = None, codes=None, scales=None):
 def w4a4_gemm(a_codes, a_scales, w_codes, w_scales, y=None):
     """bf16 [M][N] = dequant(A) * dequant(W)^T for MXFP4 A [M][K] and W [N][K]."""
     torch = _torch()
+    if a_codes.dim() != 2 or w_codes.dim() != 2 or a_codes.shape[1] != w_codes.shape[1]:
+        raise ValueError("a_codes [M][K/2] and w_codes [N][K/2] must share K")
     M, N, K = a_codes.shape[0], w_codes.shape[0], a_codes.shape[1] * 2
+    dev = a_codes.device
+    _param(a_codes, "a_codes", dev, "u8", M * (K // 2))
+    _param(a_scales, "a_scales", dev, "u8", M * (K // 32))
+    _param(w_codes, "w_codes", dev, "u8", N * (K // 2))
+    _param(w_scales, "w_scales", dev, "u8", N * (K // 32))
     if y is None:  # rows padded to a multiple of 8 elements (16-byte aligned)
         ld = (N + 7) // 8 * 8
-        y = torch.empty((M, ld), dtype=torch.bfloat16, device=a_codes.device)[:, :N]
+        y = torch.empty((M, ld), dtype=torch.bfloat16, device=dev)[:, :N]
+    _rows_out(y, "y", dev, "bf16", M, N)
     _check("kq_w4a4_gemm", kq_w4a4_gemm(
         a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
         M, N, K, y.data_ptr(), y.stride(0), _stream(a_codes)))
@@ -298,6 +358,13 @@ def _rps(tokens: int, rows_per_sample) -> int:
     return max(tokens, 1) if rows_per_sample is None else int(rows_per_sample)
 
 
+def _modulation(x, shift, scale, tokens: int, d: int, rows_per_sample) -> None:
+    rps = _rps(tokens, rows_per_sample)
+    samples = -(-tokens // rps) if rps > 0 else 0
+    _param(shift, "shift", x.device, "f32", samples * d)
+    _param(scale, "scale", x.device, "f32", samples * d)
+
+
 def adaln_transform_quant(x, shift, scale, lu, rows_per_sample=None, eps: float = 1e-6,
                           d: int | None = None, codes=None, scales=None):
     """MXFP4 of (LN(x) * (1 + scale_s) + shift_s) * T per 32-channel block, one
@@ -306,6 +373,8 @@ def adaln_transform_quant(x, shift, scale, lu, rows_per_sample=None, eps: float 
     tokens, ld = _act(x, "bf16")
     d = x.shape[1] if d is None else d
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _modulation(x, shift, scale, tokens, d, rows_per_sample)
+    _lu(lu, x.device, d)
     _check("kq_adaln_transform_quant", kq_adaln_transform_quant(
         x.data_ptr(), tokens, d, ld, shift.data_ptr(), scale.data_ptr(),
         _rps(tokens, rows_per_sample), float(eps), lu.data_ptr(), codes.data_ptr(),
@@ -319,8 +388,10 @@ def adaln_modulate(x, shift, scale, rows_per_sample=None, eps: float = 1e-6,
     torch = _torch()
     tokens, ld = _act(x, "bf16")
     d = x.shape[1] if d is None else d
+    _modulation(x, shift, scale, tokens, d, rows_per_sample)
     if h is None:
         h = torch.empty((tokens, (d + 7) // 8 * 8), dtype=torch.bfloat16, device=x.device)[:, :d]
+    _rows_out(h, "h", x.device, "bf16", tokens, d)
     _check("kq_adaln_modulate", kq_adaln_modulate(
         x.data_ptr(), tokens, d, ld, shift.data_ptr(), scale.data_ptr(),
         _rps(tokens, rows_per_sample), float(eps), h.data_ptr(), h.stride(0), _stream(x)))
@@ -334,6 +405,10 @@ def calib_objective(x, lu, gram=None, d: int | None = None, f=None):
     d = x.shape[1] if d is None else d
     if f is None:
         f = torch.empty(d // 32, dtype=torch.float32, device=x.device)
+    _param(f, "f", x.device, "f32", d // 32)
+    _lu(lu, x.device, d)
+    if gram is not None:
+        _param(gram, "gram", x.device, "f32", (d // 32) * 1024)
     _check("kq_calib_objective", kq_calib_objective(
         x.data_ptr(), tokens, d, ld, lu.data_ptr(), gram.data_ptr() if gram is not None else None,
         f.data_ptr(), _stream(x)))
@@ -350,6 +425,10 @@ def calibrate(x, lu0, noise, gram=None, sigma0: float = 0.05):
     Returns (theta [d/32][5][3], fbest [d/32], history [iterations + 1][d/32])."""
     torch = _torch()
     nb = lu0.shape[0]
+    _param(lu0, "lu0", x.device, "f32", nb * 15)
+    if noise.dim() != 3 or noise.shape[1] != nb or noise.shape[2] != 15 or noise.shape[0] < 1:
+        raise ValueError("noise must be [iterations + 1][d/32][15]")
+    _param(noise, "noise", x.device, "f32", noise.numel())
     iters = noise.shape[0] - 1
     theta = lu0.reshape(nb, 15).clone().contiguous()
     cand = theta.clone()
