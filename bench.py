@@ -86,7 +86,20 @@ rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o FETCH_SIZE -
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/WRITE_SIZE -o WRITE_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration --steps 20
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration --steps 20
+rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ -o SQ -- python3 bench.py --kernel-only --steps 20 --warmup 5
+rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_mfma -o SQ_mfma -- python3 bench.py --kernel-only --kernel kq_transform_quant_mfma --steps 20 --warmup 5
 python3 bench.py --summarize-profiles OUT"""
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _csv_rows(path):
@@ -115,12 +128,22 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
     src_hash = kernel_source_hash()
 
     stats = _csv_rows(_find(os.path.join(out_dir, "trace"), "kernel_stats.csv"))
+    # per-dispatch durations, for the median and the 90th percentile
+    durations = {}
+    for r in _csv_rows(_find(os.path.join(out_dir, "trace"), "kernel_trace.csv")):
+        durations.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def pct(name_key, q):
+        vals = sorted(v for k, vs in durations.items() if name_key in k for v in vs)
+        return vals[min(len(vals) - 1, int(q * len(vals)))] if vals else float("nan")
+
     lines = [f"# rocprofv3 --kernel-trace --stats, {workload} {w.tokens}x{w.d} bf16, one MI355X",
              f"# kernel sources {src_hash}; commands (REPO = repository root, OUT = output dir):"]
     lines += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
     lines.append(f"# algorithmic bytes per launch: {nbytes}")
-    lines.append(f"{'entry point':26s} {'calls':>6s} {'avg us':>8s} {'min us':>8s} "
-                 f"{'max us':>8s} {'GB/s(avg)':>10s}")
+    lines.append(f"{'entry point':26s} {'calls':>6s} {'avg us':>8s} {'med us':>8s} {'p90 us':>8s} "
+                 f"{'min us':>8s} {'max us':>8s} {'GB/s(avg)':>10s}")
     gemm_flops = 2.0 * w.tokens * inputs.GEMM_N * inputs.GEMM_K
     weight_bytes = inputs.GEMM_N * inputs.GEMM_K * (2 + 0.5 + 1 / 32)
     for entry, key in KERNEL_MATCH.items():
@@ -138,6 +161,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                 else:
                     rate = f"{nbytes / (avg * 1e3):10.1f}"
                 lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
+                             f"{pct(key, 0.5):8.3f} {pct(key, 0.9):8.3f} "
                              f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} {rate}")
     with open(os.path.join(PROFILES, f"kernel_stats_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -180,7 +204,31 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
             f"algorithmic bytes         {nbytes / 1e6:9.3f} MB  (ratio {(read_b + write_b) / nbytes:.4f})"]
     with open(os.path.join(PROFILES, f"hbm_traffic_kq_transform_quant_{workload}.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
-    print("\n".join(lines + txt))
+
+    # instruction counters of the hot path and of the matrix-core arm
+    ctr = [f"# SQ counters per dispatch (mean over the dispatches), {workload} "
+           f"{w.tokens}x{w.d}, from rocprofv3 --pmc",
+           f"# kernel sources {src_hash}; commands:"]
+    ctr += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma")):
+        if not os.path.isdir(os.path.join(out_dir, sub)):
+            ctr.append(f"{entry}: no {sub} pass in {out_dir}")
+            continue
+        rows = _csv_rows(_find(os.path.join(out_dir, sub), "counter_collection.csv"))
+        means = {}
+        for r in rows:
+            if KERNEL_MATCH[entry] in r["Kernel_Name"]:
+                means.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        means = {k: sum(v) / len(v) for k, v in means.items()}
+        ctr.append(f"{entry}:")
+        for k in sorted(means):
+            ctr.append(f"  {k:26s} {means[k]:14.1f}")
+        if means.get("SQ_WAVES"):
+            ctr.append(f"  VALU instructions per wave {means['SQ_INSTS_VALU'] / means['SQ_WAVES']:14.1f}")
+            ctr.append(f"  VALU lane-ops per element  {64 * means['SQ_INSTS_VALU'] / w.elements:14.2f}")
+    with open(os.path.join(PROFILES, f"counters_{workload}.txt"), "w") as f:
+        f.write("\n".join(ctr) + "\n")
+    print("\n".join(lines + txt + ctr))
     return 0
 
 
@@ -351,6 +399,22 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps  # ms per launch
 
+    def timed_one_set(fn_name, steps, warmup):
+        """The same launches on buffer set 0 every step: its inputs stay in
+        the 256 MB MALL, so this is a cache-warm figure, never the value."""
+        fn, a0 = getattr(L, fn_name), argsets(fn_name)[0]
+        for _ in range(warmup):
+            fn(*a0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn(*a0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def settle(seconds=0.3):
         """Untimed launches until the GPU clocks have left their idle state:
         the first timed batch of a fresh process otherwise runs several per
@@ -392,6 +456,10 @@ def main() -> int:
             extra[name] = {"ms_per_step": round(pms, 6),
                            "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+        wms = timed_one_set("kq_transform_quant", args.steps, args.warmup)
+        extra["mall_warm_single_buffer"] = {
+            "ms_per_step": round(wms, 6), "GBps": round(nbytes / (wms * 1e-3) / 1e9, 1),
+            "note": "one buffer set every step, inputs served from the MALL; not the value"}
         # the copy ceiling and the inverse wrote into the rotating buffers:
         # restore the inputs before the next peers read them
         for xi in xs:
@@ -493,6 +561,24 @@ def main() -> int:
                "kind": "oracle",
                "sample": f"the whole {T}x{d} workload, oracle fixed-fp32-order mode, "
                          f"median of {len(times)} runs on {cores} threads"}
+        # the same mode on one thread, and the fp64 definition mode on all
+        # threads over the first 512 rows (bounded CPU time)
+        one = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.transform_quant(x_bits, lu, oracle.STAGED32, threads=1)
+            one.append(time.perf_counter() - t0)
+        rows = min(512, T)
+        sub_bytes = nbytes * rows / T
+        dense = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.transform_quant(x_bits[:rows], lu, oracle.DENSE64, threads=cores)
+            dense.append(time.perf_counter() - t0)
+        cpu["single_thread_value"] = round(nbytes / sorted(one)[1] / 1e9, 4)
+        cpu["dense64_value"] = round(sub_bytes / sorted(dense)[1] / 1e9, 4)
+        cpu["dense64_sample"] = f"first {rows} rows, fp64 definition mode, median of 3 on {cores} threads"
+        cpu["cpu_model"] = _cpu_model()
 
     line = {
         "metric": "fused Kron-transform+MXFP4 quantize GB/s & % HBM peak, 4608x3072 bf16, 1 GPU",
