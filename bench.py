@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak
 MALL_BYTES = 256 << 20         # Infinity Cache
+ADALN_MAX_D = 8192             # channels the AdaLN-fused kernel accepts
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
 
@@ -334,8 +335,11 @@ def main() -> int:
     # stream, one sample's shift/scale; the unfused pipeline writes bf16 h.
     shift_np, scale_np = inputs.modulation(args.workload, 1, d)
     shift_d, scale_d = torch.from_numpy(shift_np).to(dev), torch.from_numpy(scale_np).to(dev)
-    need_h = (args.kernel_only and args.kernel == "kq_adaln_unfused") or \
-        not (args.kernel_only or args.no_peers)
+    if args.kernel_only and args.kernel.startswith("kq_adaln") and d > ADALN_MAX_D:
+        print(f"the AdaLN-fused kernel takes d <= {ADALN_MAX_D} channels", file=sys.stderr)
+        return 2
+    need_h = d <= ADALN_MAX_D and ((args.kernel_only and args.kernel == "kq_adaln_unfused") or
+                                   not (args.kernel_only or args.no_peers))
     hs = [torch.empty((T, d), dtype=torch.bfloat16, device=dev) for _ in range(R)] if need_h else []
 
     def argsets(fn_name):
@@ -466,14 +470,16 @@ def main() -> int:
             xi.copy_(x_keep)
         timed("kq_transform_quant", R, 0)
         # AdaLN + quantizer: fused (one pass, same bytes as the quantizer) vs
-        # modulate-to-bf16 then quantize (4 more bytes per element through HBM)
-        fms = timed("kq_adaln_transform_quant", args.steps, args.warmup)
-        ums = timed("kq_adaln_unfused", args.steps, args.warmup)
-        extra["adaln_fused"] = {"ms_per_step": round(fms, 6),
-                                "GBps": round(nbytes / (fms * 1e-3) / 1e9, 1)}
-        extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
-                                  "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
-                                  "fused_speedup": round(ums / fms, 3)}
+        # modulate-to-bf16 then quantize (4 more bytes per element through HBM);
+        # the fused kernel keeps a sample's vectors in LDS, so d <= 8192
+        if d <= ADALN_MAX_D:
+            fms = timed("kq_adaln_transform_quant", args.steps, args.warmup)
+            ums = timed("kq_adaln_unfused", args.steps, args.warmup)
+            extra["adaln_fused"] = {"ms_per_step": round(fms, 6),
+                                    "GBps": round(nbytes / (fms * 1e-3) / 1e9, 1)}
+            extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
+                                      "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
+                                      "fused_speedup": round(ums / fms, 3)}
     if not args.no_peers and d == 3072:
         # Calibration of the block parameters from the Hadamard start (per-block
         # (1+1)-ES on the MXFP4 round-trip objective): 150 iterations on 256
