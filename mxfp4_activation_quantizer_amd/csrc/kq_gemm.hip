@@ -109,9 +109,9 @@ struct DmaPlan {
     const uint8_t *sb[kDS];
 };
 
-// Tile kt of both operands into stage st.  The restrict parameter gives the
-// DMAs alias-scope metadata once inlined, which lets the compiler's wait
-// insertion tell the stages apart.
+// Tile kt of both operands into stage st (one of the three stage arrays:
+// with the stages as separate objects the compiler's wait insertion sees
+// that these DMAs do not alias reads of the other two).
 __device__ __forceinline__ void gemm_issue(const DmaPlan &pl, const uint8_t *ac, const uint8_t *wc,
                                            int kt, bool half, int wave, uint8_t *__restrict__ st) {
 #pragma unroll
