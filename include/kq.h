@@ -197,6 +197,8 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
  *
  * K % 128 == 0; M and N are arbitrary, with max(M, N) * K/2 < 2^31 (one
  * operand's codes under 2 GiB).  M == 0 or N == 0 returns KQ_OK.
+ * KQ_ERR_HIP also if the library was built so that the kernel needs scratch
+ * memory (its load waits count its own loads and would be wrong then).
  */
 kq_status kq_w4a4_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
                        const uint8_t *w_codes, const uint8_t *w_scales, int64_t M, int64_t N,

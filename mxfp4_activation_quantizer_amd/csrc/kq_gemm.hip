@@ -351,6 +351,15 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
     const void *fn = (const void *)w4a4_gemm_kernel;
+    // The explicit vmcnt waits count this kernel's DMAs; register spills would
+    // add scratch loads and stores to that count and let a stage be read
+    // before it has landed.  A build that gives the kernel scratch memory is
+    // refused rather than run.
+    static const bool no_scratch = [fn] {
+        hipFuncAttributes fa;
+        return hipFuncGetAttributes(&fa, fn) == hipSuccess && fa.localSizeBytes == 0;
+    }();
+    if (!no_scratch) return KQ_ERR_HIP;
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,
                                          (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
