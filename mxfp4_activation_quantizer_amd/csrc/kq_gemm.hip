@@ -183,6 +183,98 @@ __device__ __forceinline__ void gemm_compute(const uint8_t *__restrict__ b, int 
     }
 }
 
+// Workgroup tile lin of the order that walks four M tiles for each N tile.
+__device__ __forceinline__ void tile_origin(int lin, int mtc, int ntc, int &m0, int &n0) {
+    const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
+    const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
+    const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
+    m0 = mt * kBM;
+    n0 = nt * kBN;
+}
+
+// This lane's DMA sources for the tile at (m0, n0): a 1 KB region is 8 rows
+// of 128 bytes; lane p of it fetches the chunk that slot p & 7 of row p >> 3
+// holds.  Rows past M or N repeat the last row.
+__device__ __forceinline__ void make_plan(DmaPlan &pl, int m0, int n0, int M, int N, int K2, int K32,
+                                          int wave, int lane, const uint8_t *as, const uint8_t *ws) {
+#pragma unroll
+    for (int q = 0; q < kDA; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the A tile
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
+        pl.hia[q] = c >= 4;
+    }
+#pragma unroll
+    for (int q = 0; q < kDW; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
+        pl.hiw[q] = c >= 4;
+    }
+#pragma unroll
+    for (int q = 0; q < kDS; ++q) {
+        int r = q * (kGemmThreads / 64) + wave;
+        r = r < kDSRegions ? r : r - (kGemmThreads / 64);  // past the last: a repeat
+        pl.rs[q] = r;
+        const int dw = r * 64 + lane, v = dw >> 1, hf = dw & 1;  // row slot, dword of its 8 bytes
+        const int ra = m0 + v < M ? m0 + v : M - 1;
+        const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
+        pl.sb[q] = v < kBM ? as : ws;
+        pl.gs[q] = (v < kBM ? ra : rw) * K32 + 4 * hf;
+        pl.his[q] = hf;
+    }
+}
+
+// Output rows [r0, r0 + 64) of the tile at (m0, n0), bf16 (nearest even),
+// through LDS buffer ob (64 rows x 512 bytes): the waves holding those rows
+// write them in the 8-byte slot layout (c / 4) ^ (r & 31), then every thread
+// stores 16 bytes, two whole rows per wave instruction.  The caller places
+// a barrier between the write and the read phase (barrier_mid) and after the
+// reads before ob is reused.
+template <class Barrier>
+__device__ __forceinline__ void store_rows64(const f32x16g (&acc)[2][2], int r0, uint8_t *ob,
+                                             int wm, int wn, int i32, int kg, int tid, int m0,
+                                             int n0, int M, int N, int64_t ldy, uint16_t *y,
+                                             Barrier barrier_mid) {
+    if (wm * 64 == r0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int lr = j * 32 + i32;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int s8 = wn * 16 + i * 8 + 2 * q + kg;
+                    const uint32_t lo = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
+                    const uint32_t hi = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
+                    *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
+                }
+            }
+        }
+    }
+    barrier_mid();
+    constexpr int kRowChunks = kBN * 2 / 16;
+#pragma unroll
+    for (int k = 0; k < 64 * kRowChunks / kGemmThreads; ++k) {
+        const int f = tid + k * kGemmThreads;
+        const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * (kBN * 2) + 16 * (ch ^ (g >> 1)));
+        if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int gr = m0 + r0 + row, col = n0 + 8 * ch;
+        if (gr >= M || col >= N) continue;
+        uint16_t *yp = y + (int64_t)gr * ldy + col;
+        if (col + 7 < N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yp));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (col + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
@@ -326,6 +418,92 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined form for K a multiple of three K tiles (K % 768 == 0): every
+// output tile then starts at stage 0, K tile k of any tile sits in stage
+// k % 3, and the pipeline runs on across output tiles.  The last two steps
+// of a tile issue the next tile's first two K tiles, and the epilogue runs
+// in stage 2 (its last K tile's, free once multiplied) while those are in
+// flight: no pipeline fill per tile and no idle epilogue.
+// Waits per step as above: vmcnt(one tile's DMAs) then a barrier.  At a
+// tile's first two steps the outstanding operations also include the
+// previous epilogue's stores, which are younger than the K tile waited
+// for, so the same count still retires it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
+    const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldy, int mtc, int ntc) {
+    const int tiles = mtc * ntc, per = (tiles + 7) / 8, wpx = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7;
+    int t = blockIdx.x >> 3;
+    if (t >= per || xcd * per + t >= tiles) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kGemmWN, wn = wave % kGemmWN;
+    const int i32 = lane & 31, kg = lane >> 5;
+    const int K2 = K / 2, K32 = K / 32;
+    const int KT = K / kBK;  // a multiple of 3, no half tile
+
+    int m0, n0;
+    tile_origin(xcd * per + t, mtc, ntc, m0, n0);
+    DmaPlan pc;
+    make_plan(pc, m0, n0, M, N, K2, K32, wave, lane, as, ws);
+    gemm_issue(pc, ac, wc, 0, false, wave, gemm_st0);
+    gemm_issue(pc, ac, wc, 1, false, wave, gemm_st1);
+
+    f32x16g acc[2][2];
+    auto barrier = [] { __builtin_amdgcn_s_barrier(); };
+    for (;;) {
+        // the next tile of this workgroup, if any (else the DMAs of the last
+        // two steps repeat this tile's first K tiles, never read)
+        const int tn = t + wpx;
+        const bool has_next = tn < per && xcd * per + tn < tiles;
+        int m1 = m0, n1 = n0;
+        if (has_next) tile_origin(xcd * per + tn, mtc, ntc, m1, n1);
+        DmaPlan pn;
+        make_plan(pn, m1, n1, M, N, K2, K32, wave, lane, as, ws);
+
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
+
+        // step s: retire K tile s, issue K tile s + 2 (or the next tile's
+        // s + 2 - KT) into stage (s + 2) % 3, multiply K tile s from stage s % 3
+        constexpr int kSteps = 15;
+        for (int s0 = 0; s0 < KT; s0 += kSteps) {
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int st = s0 + u;
+                if (st >= KT) break;
+                uint8_t *in = u % 3 == 1 ? gemm_st0 : u % 3 == 2 ? gemm_st1 : gemm_st2;
+                const uint8_t *rd = u % 3 == 0 ? gemm_st0 : u % 3 == 1 ? gemm_st1 : gemm_st2;
+                KQ_WAIT_VM(kDPerTile);
+                __builtin_amdgcn_s_barrier();
+                if (st + 2 < KT) gemm_issue(pc, ac, wc, st + 2, false, wave, in);
+                else gemm_issue(pn, ac, wc, st + 2 - KT, false, wave, in);
+                gemm_compute(rd, kBK / 64, wm, wn, i32, kg, acc);
+            }
+        }
+        // epilogue in stage 2 (K tile KT - 1's, KT a multiple of 3), two
+        // passes of 64 rows; stages 0 and 1 take the next tile's first K tiles
+        __builtin_amdgcn_s_barrier();
+        store_rows64(acc, 0, gemm_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        __builtin_amdgcn_s_barrier();
+        store_rows64(acc, 64, gemm_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        if (!has_next) break;
+        t = tn;
+        m0 = m1;
+        n0 = n1;
+        pc = pn;
+    }
+    // the last repeats may still be landing in LDS: finish before the
+    // workgroup's LDS is handed to another
+    KQ_WAIT_VM(0);
+}
+
 static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t *wc,
                              const uint8_t *ws, uint16_t *y, int M, int N, int K, int64_t ldy,
                              void *stream) {
@@ -350,14 +528,19 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     const int64_t grid = 8 * (per < wpx ? per : wpx);
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
-    const void *fn = (const void *)w4a4_gemm_kernel;
+    static const int pipe_env = env_override("KQ_GEMM_PIPE", 1, [](int v) { return v == 0 || v == 1; });
+    const bool pipe = pipe_env && K % (3 * kBK) == 0;
+    const void *fn = pipe ? (const void *)w4a4_gemm_pipe_kernel : (const void *)w4a4_gemm_kernel;
     // The explicit vmcnt waits count this kernel's DMAs; register spills would
     // add scratch loads and stores to that count and let a stage be read
     // before it has landed.  A build that gives the kernel scratch memory is
     // refused rather than run.
-    static const bool no_scratch = [fn] {
-        hipFuncAttributes fa;
-        return hipFuncGetAttributes(&fa, fn) == hipSuccess && fa.localSizeBytes == 0;
+    static const bool no_scratch = [] {
+        hipFuncAttributes fa, fb;
+        return hipFuncGetAttributes(&fa, (const void *)w4a4_gemm_kernel) == hipSuccess &&
+               fa.localSizeBytes == 0 &&
+               hipFuncGetAttributes(&fb, (const void *)w4a4_gemm_pipe_kernel) == hipSuccess &&
+               fb.localSizeBytes == 0;
     }();
     if (!no_scratch) return KQ_ERR_HIP;
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,

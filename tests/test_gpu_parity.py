@@ -599,7 +599,11 @@ def _random_mxfp4(g, rows, k, lo=118, hi=128):
                                    (1, 17, 128), (257, 129, 512),
                                    # K past one 15-step pass of the K pipeline
                                    # (3328), whole and ending in a half tile
-                                   (70, 260, 4096), (33, 40, 4224), (5, 8, 7808)])
+                                   (70, 260, 4096), (33, 40, 4224), (5, 8, 7808),
+                                   # K a multiple of 768: the cross-tile
+                                   # pipelined kernel (6912: two loop passes)
+                                   (130, 300, 768), (257, 513, 1536), (5, 17, 2304),
+                                   (64, 256, 6912)])
 def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     torch = torch_cuda
     g = np.random.default_rng(M * 7 + N * 3 + K)
@@ -611,7 +615,8 @@ def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     _assert_gemm_close(yb, Y, B, K)
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8)])
+@pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8),
+                                       (70, 260, 768, 12)])
 def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     """Row stride beyond N: the whole-row epilogue writes only columns < N
     of rows < M; the padding keeps its sentinel."""
@@ -626,6 +631,23 @@ def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     Y, B = _gemm_reference(ac, as_, wc, ws)
     _assert_gemm_close(yb[:, :N], Y, B, K)
     assert (inputs.bf16_bits_to_f32(yb[:, N:]) == 5.0).all()
+
+
+def test_gemm_workgroups_walk_several_tiles(torch_cuda):
+    """More output tiles (20 x 16 = 320) than workgroups (one per CU): the
+    persistent workgroups carry the K pipeline from one tile into the next
+    (K = 768, the pipelined kernel).  Three rows of every M tile are checked
+    over all N columns."""
+    torch = torch_cuda
+    M, N, K = 2560, 4096, 768
+    g = np.random.default_rng(77)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    rows = np.array([mt * 128 + r for mt in range(M // 128) for r in (0, 61, 127)])
+    Y, B = _gemm_reference(ac[rows], as_[rows], wc, ws)
+    _assert_gemm_close(yb[rows], Y, B, K)
 
 
 def test_gemm_full_size_sampled_rows(torch_cuda):
