@@ -73,7 +73,7 @@ KERNEL_MATCH = {
     "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
-    "kq_w4a4_gemm": "w4a4_gemm_kernel",
+    "kq_w4a4_gemm": "w4a4_gemm_",  # the per-tile and the cross-tile pipelined kernel
     "kq_adaln_transform_quant": "adaln_kernel<1, true>",
     "kq_adaln_modulate": "adaln_kernel<1, false>",
     "kq_calib_objective": "calib_objective_kernel",
