@@ -92,6 +92,65 @@ rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ
 python3 bench.py --summarize-profiles OUT"""
 
 
+def oracle_peer_times(oracle, workload: str, x_bits, lu, mult, threads: int) -> dict:
+    """The oracle function of each peer entry point timed on a bounded
+    sample of the same workload (median of 3 runs on ``threads`` threads),
+    in the unit the peer reports: GB/s of its algorithmic bytes, GFLOP/s for
+    the GEMM.  Reported beside the GPU figures; never a target."""
+    import numpy as np
+    from mxfp4_activation_quantizer_amd import inputs
+    w = inputs.WORKLOADS[workload]
+    d = w.d
+    rows = min(1024, w.tokens)
+    xs = x_bits[:rows]
+    elem = rows * d
+    bpe = 2 + 0.5 + 1 / 32  # bytes per element, both directions
+
+    def med(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    def rec(value, unit, sample):
+        return {"value": round(value, 4), "unit": unit, "threads": threads, "sample": sample}
+
+    out = {}
+    tag = f"first {rows} rows of {workload}"
+    t = med(lambda: oracle.smooth_quant(xs, mult, threads=threads))
+    out["smooth_quant"] = rec(elem * bpe / t / 1e9, "GB/s", tag)
+    t = med(lambda: oracle.fwht32_quant(xs, threads=threads))
+    out["fwht32_quant"] = rec(elem * bpe / t / 1e9, "GB/s", tag)
+    t = med(lambda: oracle.transform_quant(xs, lu, oracle.DENSE64, threads=threads))
+    out["transform_quant_mfma"] = rec(elem * bpe / t / 1e9, "GB/s", tag + ", fp64 definition mode")
+    codes, scales = oracle.transform_quant(xs, lu, oracle.STAGED32, threads=threads)
+    t = med(lambda: oracle.dequant_inverse(codes, scales, lu, threads=threads))
+    out["dequant_inverse"] = rec(elem * bpe / t / 1e9, "GB/s", tag)
+    if d <= ADALN_MAX_D:
+        shift, scale = inputs.modulation(workload, 1, d)
+        t = med(lambda: oracle.adaln_transform_quant(xs, shift, scale, lu, rows_per_sample=rows,
+                                                     threads=threads))
+        out["adaln_fused"] = rec(elem * bpe / t / 1e9, "GB/s", tag)
+    if d == inputs.GEMM_K:
+        wb = inputs.gemm_weight()
+        t = med(lambda: oracle.weight_quant(wb[:rows], lu, threads=threads))
+        out["weight_quant"] = rec(rows * d * bpe / t / 1e9, "GB/s", f"first {rows} weight rows")
+        wc, wsc = oracle.weight_quant(wb, lu, threads=threads)
+        W = oracle.mxfp4_dequant(wc, wsc)
+        a_rows = 16
+        A = oracle.mxfp4_dequant(codes[:a_rows], scales[:a_rows])
+        t = med(lambda: oracle.matmul_nt(A, W, threads=threads))
+        out["w4a4_gemm"] = rec(2.0 * a_rows * W.shape[0] * d / t / 1e9, "GFLOP/s",
+                               f"{a_rows} activation rows x {W.shape[0]} x {d}, fp64 products")
+        cal = x_bits[:256]
+        t = med(lambda: oracle.calib_objective(cal, lu, threads=threads))
+        out["calibration"] = {"value": round(t * 1e3, 3), "unit": "ms per objective evaluation",
+                              "threads": threads, "sample": "256 calibration rows"}
+    return out
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -457,8 +516,9 @@ def main() -> int:
                               ("copy_ceiling", "kq_copy_ceiling"),
                               ("dequant_inverse", "kq_dequant_inverse")]:
             pms = timed(fn_name, args.steps, args.warmup)
-            extra[name] = {"ms_per_step": round(pms, 6),
-                           "GBps": round(nbytes / (pms * 1e-3) / 1e9, 1)}
+            pg = nbytes / (pms * 1e-3) / 1e9
+            extra[name] = {"ms_per_step": round(pms, 6), "GBps": round(pg, 1),
+                           "frac_of_hbm_peak": round(pg / PEAK_HBM_GBS, 4)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
         wms = timed_one_set("kq_transform_quant", args.steps, args.warmup)
         extra["mall_warm_single_buffer"] = {
@@ -476,7 +536,8 @@ def main() -> int:
             fms = timed("kq_adaln_transform_quant", args.steps, args.warmup)
             ums = timed("kq_adaln_unfused", args.steps, args.warmup)
             extra["adaln_fused"] = {"ms_per_step": round(fms, 6),
-                                    "GBps": round(nbytes / (fms * 1e-3) / 1e9, 1)}
+                                    "GBps": round(nbytes / (fms * 1e-3) / 1e9, 1),
+                                    "frac_of_hbm_peak": round(nbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
                                       "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
                                       "fused_speedup": round(ums / fms, 3)}
@@ -511,8 +572,9 @@ def main() -> int:
     if gemm:
         timed("kq_transform_quant", R, 0)  # A operands: fresh quantizer outputs
         pms = timed("kq_weight_quant", max(10, args.steps // 10), max(2, args.warmup // 10))
+        wg = gemm["weight_bytes"] / (pms * 1e-3) / 1e9
         extra["weight_quant"] = {"ms_per_step": round(pms, 6), "shape": [gemm["n"], gemm["k"]],
-                                 "GBps": round(gemm["weight_bytes"] / (pms * 1e-3) / 1e9, 1)}
+                                 "GBps": round(wg, 1), "frac_of_hbm_peak": round(wg / PEAK_HBM_GBS, 4)}
         pms = timed("kq_w4a4_gemm", max(10, args.steps // 10), max(2, args.warmup // 10))
         tf = gemm["flops"] / (pms * 1e-3) / 1e12
         if "theta" in gemm:
@@ -585,6 +647,8 @@ def main() -> int:
         cpu["dense64_value"] = round(sub_bytes / sorted(dense)[1] / 1e9, 4)
         cpu["dense64_sample"] = f"first {rows} rows, fp64 definition mode, median of 3 on {cores} threads"
         cpu["cpu_model"] = _cpu_model()
+        if not args.no_peers:
+            cpu["peers"] = oracle_peer_times(oracle, args.workload, x_bits, lu, mult, cores)
 
     line = {
         "metric": "fused Kron-transform+MXFP4 quantize GB/s & % HBM peak, 4608x3072 bf16, 1 GPU",
