@@ -78,6 +78,7 @@ KERNEL_MATCH = {
     "kq_adaln_modulate": "adaln_kernel<1, false>",
     "kq_calib_objective": "calib_objective_kernel",
     "kq_calib_es_update": "calib_es_update_kernel",
+    "kq_calib_es_step": "calib_es_step_kernel",
 }
 
 PROFILE_COMMANDS = """\
@@ -216,6 +217,8 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                     rate = f"{weight_bytes / (avg * 1e3):10.1f} ({inputs.GEMM_N}x{inputs.GEMM_K} weight)"
                 elif entry == "kq_adaln_modulate":
                     rate = f"{4 * w.elements / (avg * 1e3):10.1f} (bf16 in, bf16 out)"
+                elif entry == "kq_calib_es_update":
+                    rate = f"{'':>10s} (update alone, {w.d // 32} blocks)"
                 elif entry.startswith("kq_calib"):
                     rate = f"{'':>10s} (one candidate set, 256 x {w.d} calibration rows)"
                 else:

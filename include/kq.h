@@ -283,6 +283,38 @@ kq_status kq_calib_es_update(int64_t nb, float *theta, float *sigma, float *fbes
                              const float *fcand, const float *noise, void *stream);
 
 /*
+ * kq_calib_es_step — one whole iteration of the calibration in one launch:
+ * the same result, bit for bit, as kq_calib_objective on cand (writing
+ * fcand) followed by kq_calib_es_update with that fcand, for every block.
+ * The update of block j depends only on block j's objective, so each block's
+ * workgroup applies it as soon as its own sum is known.
+ *   x, tokens, d, ld_x, gram   as for kq_calib_objective
+ *   theta, sigma, fbest, cand, noise   as for kq_calib_es_update, nb = d/32
+ *   fhist  fp32 [d/32] (written with the kept objectives after the update),
+ *          or NULL
+ * The candidate's objective itself is not stored.  Errors as for the two
+ * separate calls.
+ */
+kq_status kq_calib_es_step(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                           const float *gram, float *theta, float *sigma, float *fbest,
+                           float *cand, const float *noise, float *fhist, void *stream);
+
+/*
+ * kq_calib_es_run — `iterations` calls of kq_calib_es_step issued from the
+ * library in one call, so a long calibration is not paced by the caller's
+ * per-launch overhead:
+ *   noise  fp32 [iterations][d/32][15]; iteration i uses noise + i*(d/32)*15
+ *   fhist  fp32 [iterations][d/32], row i written after iteration i, or NULL
+ * Other arguments as for kq_calib_es_step.  iterations == 0 does nothing;
+ * iterations < 0 or above 2^24 is KQ_ERR_SHAPE.  The launches are queued on
+ * `stream` and the call returns without waiting.  If a launch fails,
+ * KQ_ERR_HIP is returned and the state holds the iterations queued before it.
+ */
+kq_status kq_calib_es_run(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          const float *gram, float *theta, float *sigma, float *fbest, float *cand,
+                          const float *noise, int64_t iterations, float *fhist, void *stream);
+
+/*
  * kq_copy_ceiling — not a quantizer: moves the same bytes as
  * kq_transform_quant (reads the bf16 tensor, writes d/2 + d/32 bytes per row)
  * with almost no arithmetic, to measure the achievable bandwidth of this

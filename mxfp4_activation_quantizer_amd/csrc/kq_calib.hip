@@ -38,34 +38,55 @@ __device__ __forceinline__ float cal_wave_sum(float a) {
     return a;
 }
 
-__global__ __launch_bounds__(kCalThreads) void calib_objective_kernel(
-    const uint16_t *__restrict__ x, int64_t ld, int64_t tokens, const float *__restrict__ lu,
-    const float *__restrict__ gram, float *__restrict__ f) {
+__device__ __forceinline__ void load15(const float *src, float (&v)[15]) {
+#pragma unroll
+    for (int i = 0; i < 15; ++i) v[i] = src[i];
+}
+
+__device__ __forceinline__ void load_row32(const uint16_t *src, u32x4 (&v)[4]) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p[i];
+}
+
+// Objective of block j = blockIdx.x over all tokens, for the parameters pr
+// (the block's 15 values, already in registers); the total lands in thread 0
+// (the other threads return an unspecified partial value).  Each thread's
+// next token is loaded one iteration ahead, the first one before the
+// parameter set-up.
+__device__ __forceinline__ float calib_block_objective(const uint16_t *__restrict__ x, int64_t ld,
+                                                       int64_t tokens, const float (&pr)[15],
+                                                       const float *__restrict__ gram) {
     __shared__ float G[32 * 32];
     __shared__ float wsum[kCalThreads / 64];
     const int j = blockIdx.x, tid = threadIdx.x;
+    const uint16_t *xb = x + (int64_t)j * 32;
+    u32x4 nx[4] = {};
+    if (tid < tokens) load_row32(xb + (int64_t)tid * ld, nx);
     if (gram) {
         for (int i = tid; i < 1024; i += kCalThreads) G[i] = gram[(int64_t)j * 1024 + i];
     }
-    KronStage fw = KronStage::from(lu);
-    KronInverseStage iv = KronInverseStage::from(lu);
-    fw.fetch(j);
-    iv.fetch(j);
+    KronStage fw = KronStage::from(nullptr);
+    KronInverseStage iv = KronInverseStage::from(nullptr);
+#pragma unroll
+    for (int i = 0; i < 15; ++i) fw.p[i] = iv.p[i] = pr[i];
     fw.setup();
     iv.setup();
     __syncthreads();
 
     float acc = 0.0f;
     for (int64_t t = tid; t < tokens; t += kCalThreads) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(x + t * ld + (int64_t)j * 32);
+        u32x4 cur[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nx[i];
+        if (t + kCalThreads < tokens) load_row32(xb + (t + kCalThreads) * ld, nx);
         float xv[32], z[32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const u32x4 v = p[i];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                xv[8 * i + 2 * c] = bf16_lo(v[c]);
-                xv[8 * i + 2 * c + 1] = bf16_hi(v[c]);
+                xv[8 * i + 2 * c] = bf16_lo(cur[i][c]);
+                xv[8 * i + 2 * c + 1] = bf16_hi(cur[i][c]);
             }
         }
 #pragma unroll
@@ -95,48 +116,102 @@ __global__ __launch_bounds__(kCalThreads) void calib_objective_kernel(
     acc = cal_wave_sum(acc);
     if ((tid & 63) == 0) wsum[tid >> 6] = acc;
     __syncthreads();
-    if (tid == 0) {
-        float s = wsum[0];
+    float s = wsum[0];
 #pragma unroll
-        for (int w = 1; w < kCalThreads / 64; ++w) s = s + wsum[w];
-        f[j] = s;
-    }
+    for (int w = 1; w < kCalThreads / 64; ++w) s = s + wsum[w];
+    return s;
 }
 
-// One (1+1)-ES step per block, in this fp32 order: accept the evaluated
-// candidate if it is strictly better (sigma * 1.5, at most 0.5), otherwise
-// sigma * 0.90360200 (1.5^-1/4, at least 1e-4), so that one success in five
-// keeps sigma fixed; then the next candidate fma(sigma, noise, theta), kept
-// at theta when any u would come within 0.1 of zero.
-__global__ void calib_es_update_kernel(int nb, float *__restrict__ theta, float *__restrict__ sigma,
-                                       float *__restrict__ fbest, float *__restrict__ cand,
-                                       const float *__restrict__ fcand,
-                                       const float *__restrict__ noise) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= nb) return;
-    float *th = theta + (int64_t)j * 15, *cd = cand + (int64_t)j * 15;
-    const float *nz = noise + (int64_t)j * 15;
-    float s = sigma[j];
-    if (fcand[j] < fbest[j]) {
+__global__ __launch_bounds__(kCalThreads) void calib_objective_kernel(
+    const uint16_t *__restrict__ x, int64_t ld, int64_t tokens, const float *__restrict__ lu,
+    const float *__restrict__ gram, float *__restrict__ f) {
+    float pr[15];
+    load15(lu + (int64_t)blockIdx.x * 15, pr);
+    const float s = calib_block_objective(x, ld, tokens, pr, gram);
+    if (threadIdx.x == 0) f[blockIdx.x] = s;
+}
+
+// One (1+1)-ES step of one block on values in registers, in this fp32 order:
+// keep the evaluated candidate cd if its objective fc is strictly below the
+// kept fb (sigma * 1.5, at most 0.5), otherwise sigma * 0.90360200
+// (1.5^-1/4, at least 1e-4), so that one success in five keeps sigma fixed;
+// then the next candidate fma(sigma, noise, theta), or theta itself when any
+// u would come within 0.1 of zero.  Returns whether cd was kept (th then
+// holds it).
+__device__ __forceinline__ bool es_update_regs(float fc, float fb, float &s, float (&th)[15],
+                                               const float (&cd)[15], const float (&nz)[15],
+                                               float (&next)[15]) {
+    const bool keep = fc < fb;
+    if (keep) {
 #pragma unroll
         for (int i = 0; i < 15; ++i) th[i] = cd[i];
-        fbest[j] = fcand[j];
         s = s * 1.5f;
         s = s < 0.5f ? s : 0.5f;
     } else {
         s = s * 0.90360200f;
         s = s > 1e-4f ? s : 1e-4f;
     }
-    sigma[j] = s;
-    float c[15];
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < 15; ++i) {
-        c[i] = __builtin_fmaf(s, nz[i], th[i]);
-        if (i % 3 == 1 && __builtin_fabsf(c[i]) < 0.1f) ok = false;
+        next[i] = __builtin_fmaf(s, nz[i], th[i]);
+        if (i % 3 == 1 && __builtin_fabsf(next[i]) < 0.1f) ok = false;
     }
 #pragma unroll
-    for (int i = 0; i < 15; ++i) cd[i] = ok ? c[i] : th[i];
+    for (int i = 0; i < 15; ++i) next[i] = ok ? next[i] : th[i];
+    return keep;
+}
+
+// Writes the outcome of es_update_regs for block j.
+__device__ __forceinline__ void es_store(int j, bool keep, float fc, float s, const float (&th)[15],
+                                         const float (&next)[15], float *theta, float *sigma,
+                                         float *fbest, float *cand) {
+    if (keep) {
+#pragma unroll
+        for (int i = 0; i < 15; ++i) theta[(int64_t)j * 15 + i] = th[i];
+        fbest[j] = fc;
+    }
+    sigma[j] = s;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) cand[(int64_t)j * 15 + i] = next[i];
+}
+
+__global__ void calib_es_update_kernel(int nb, float *__restrict__ theta, float *__restrict__ sigma,
+                                       float *__restrict__ fbest, float *__restrict__ cand,
+                                       const float *__restrict__ fcand,
+                                       const float *__restrict__ noise) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= nb) return;
+    float th[15], cd[15], nz[15], next[15];
+    load15(theta + (int64_t)j * 15, th);
+    load15(cand + (int64_t)j * 15, cd);
+    load15(noise + (int64_t)j * 15, nz);
+    float s = sigma[j];
+    const float fc = fcand[j];
+    const bool keep = es_update_regs(fc, fbest[j], s, th, cd, nz, next);
+    es_store(j, keep, fc, s, th, next, theta, sigma, fbest, cand);
+}
+
+// One whole iteration: block j's workgroup scores cand_j, then its thread 0
+// applies the update of block j (which touches only block j's entries) and
+// records the kept objective.  Everything the update reads is loaded at the
+// start, so its latency hides behind the objective, and every write comes
+// after the workgroup's last barrier.
+__global__ __launch_bounds__(kCalThreads) void calib_es_step_kernel(
+    const uint16_t *__restrict__ x, int64_t ld, int64_t tokens, const float *__restrict__ gram,
+    float *theta, float *sigma, float *fbest, float *cand, const float *noise, float *fhist) {
+    const int j = blockIdx.x;
+    float cd[15], th[15], nz[15], next[15];
+    load15(cand + (int64_t)j * 15, cd);
+    load15(theta + (int64_t)j * 15, th);
+    load15(noise + (int64_t)j * 15, nz);
+    float s = sigma[j];
+    const float fb = fbest[j];
+    const float fc = calib_block_objective(x, ld, tokens, cd, gram);
+    if (threadIdx.x != 0) return;
+    const bool keep = es_update_regs(fc, fb, s, th, cd, nz, next);
+    es_store(j, keep, fc, s, th, next, theta, sigma, fbest, cand);
+    if (fhist) fhist[j] = keep ? fc : fb;
 }
 
 }  // namespace kq
@@ -160,6 +235,40 @@ kq_status kq_calib_objective(const void *x, int64_t tokens, int64_t d, int64_t l
     const hipError_t e = hipLaunchKernel((const void *)calib_objective_kernel, dim3(nb),
                                          dim3(kCalThreads), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+kq_status kq_calib_es_run(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                          const float *gram, float *theta, float *sigma, float *fbest, float *cand,
+                          const float *noise, int64_t iterations, float *fhist, void *stream) {
+    if (tokens < 0 || tokens >= (int64_t(1) << 30) || d <= 0 || d % 32 != 0 ||
+        d > (int64_t(1) << 26) || ld_x < d || iterations < 0 || iterations > (int64_t(1) << 24))
+        return KQ_ERR_SHAPE;
+    if (iterations == 0) return KQ_OK;
+    if (!theta || !sigma || !fbest || !cand || !noise || (tokens > 0 && !x)) return KQ_ERR_NULL;
+    if (((uintptr_t)x % 16) || (ld_x * 2) % 16 || ((uintptr_t)gram % 4) ||
+        ((uintptr_t)theta % 4) || ((uintptr_t)sigma % 4) || ((uintptr_t)fbest % 4) ||
+        ((uintptr_t)cand % 4) || ((uintptr_t)noise % 4) || ((uintptr_t)fhist % 4))
+        return KQ_ERR_ALIGN;
+    const int nb = (int)(d / 32);
+    const uint16_t *xp = (const uint16_t *)x;
+    for (int64_t i = 0; i < iterations; ++i) {
+        const float *nz = noise + i * nb * 15;
+        float *fh = fhist ? fhist + i * nb : nullptr;
+        void *args[] = {(void *)&xp,    (void *)&ld_x,  (void *)&tokens, (void *)&gram,
+                        (void *)&theta, (void *)&sigma, (void *)&fbest,  (void *)&cand,
+                        (void *)&nz,    (void *)&fh};
+        const hipError_t e = hipLaunchKernel((const void *)calib_es_step_kernel, dim3(nb),
+                                             dim3(kCalThreads), args, 0, (hipStream_t)stream);
+        if (e != hipSuccess) return KQ_ERR_HIP;
+    }
+    return KQ_OK;
+}
+
+kq_status kq_calib_es_step(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                           const float *gram, float *theta, float *sigma, float *fbest,
+                           float *cand, const float *noise, float *fhist, void *stream) {
+    return kq_calib_es_run(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise, 1, fhist,
+                           stream);
 }
 
 kq_status kq_calib_es_update(int64_t nb, float *theta, float *sigma, float *fbest, float *cand,

@@ -46,6 +46,8 @@ SIGNATURES = {
                                 _P]),
     "kq_calib_objective": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_calib_es_update": (_ST, [_I64, _P, _P, _P, _P, _P, _P, _P]),
+    "kq_calib_es_step": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kq_calib_es_run": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -146,6 +148,18 @@ def kq_calib_objective(x, tokens, d, ld_x, lu, gram, f, stream=None) -> int:
 
 def kq_calib_es_update(nb, theta, sigma, fbest, cand, fcand, noise, stream=None) -> int:
     return lib().kq_calib_es_update(nb, theta, sigma, fbest, cand, fcand, noise, stream)
+
+
+def kq_calib_es_step(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise, fhist,
+                     stream=None) -> int:
+    return lib().kq_calib_es_step(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise,
+                                  fhist, stream)
+
+
+def kq_calib_es_run(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise, iterations, fhist,
+                    stream=None) -> int:
+    return lib().kq_calib_es_run(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise,
+                                 iterations, fhist, stream)
 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
@@ -421,14 +435,20 @@ def calibrate(x, lu0, noise, gram=None, sigma0: float = 0.05):
 
     ``noise`` is a float32 GPU tensor [iterations + 1][d/32][15] of standard
     normal draws (the first proposes the first candidate).  Each iteration is
-    two launches: kq_calib_objective on the candidates, kq_calib_es_update.
-    Returns (theta [d/32][5][3], fbest [d/32], history [iterations + 1][d/32])."""
+    one fused launch (objective of the candidates, then the update), all of
+    them queued by one kq_calib_es_run call.  Returns (theta [d/32][5][3], fbest [d/32],
+    history [iterations + 1][d/32])."""
     torch = _torch()
+    tokens, ld = _act(x, "bf16")
     nb = lu0.shape[0]
+    if x.shape[1] != nb * 32:
+        raise ValueError(f"x has {x.shape[1]} channels, lu0 holds {nb} blocks of 32")
     _param(lu0, "lu0", x.device, "f32", nb * 15)
     if noise.dim() != 3 or noise.shape[1] != nb or noise.shape[2] != 15 or noise.shape[0] < 1:
         raise ValueError("noise must be [iterations + 1][d/32][15]")
     _param(noise, "noise", x.device, "f32", noise.numel())
+    if gram is not None:
+        _param(gram, "gram", x.device, "f32", nb * 1024)
     iters = noise.shape[0] - 1
     theta = lu0.reshape(nb, 15).clone().contiguous()
     cand = theta.clone()
@@ -441,10 +461,9 @@ def calibrate(x, lu0, noise, gram=None, sigma0: float = 0.05):
     _check("kq_calib_es_update", kq_calib_es_update(
         nb, theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
         fcand.data_ptr(), noise[0].data_ptr(), st))
-    for i in range(iters):
-        calib_objective(x, cand, gram, f=fcand)
-        _check("kq_calib_es_update", kq_calib_es_update(
-            nb, theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
-            fcand.data_ptr(), noise[i + 1].data_ptr(), st))
-        history[i + 1].copy_(fbest)
+    if iters:
+        _check("kq_calib_es_run", kq_calib_es_run(
+            x.data_ptr(), tokens, nb * 32, ld, gram.data_ptr() if gram is not None else None,
+            theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
+            noise[1].data_ptr(), iters, history[1].data_ptr(), st))
     return theta.reshape(nb, 5, 3), fbest, history

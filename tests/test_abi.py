@@ -155,6 +155,22 @@ def test_calibration_argument_checks():
     assert u(4, None, A16, A16, A16, A16, A16) == kq.KQ_ERR_NULL
     assert u(4, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_NULL
     assert u(4, A16, A16 + 2, A16, A16, A16, A16) == kq.KQ_ERR_ALIGN
+    e = kq.kq_calib_es_step
+    assert e(A16, 4, 48, 64, None, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_SHAPE   # d % 32
+    assert e(A16, 4, 64, 32, None, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_SHAPE   # ld < d
+    assert e(A16, -1, 64, 64, None, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_SHAPE
+    assert e(None, 4, 64, 64, None, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_NULL
+    assert e(A16, 4, 64, 64, None, None, A16, A16, A16, A16, None) == kq.KQ_ERR_NULL
+    assert e(A16, 4, 64, 64, None, A16, A16, A16, A16, None, None) == kq.KQ_ERR_NULL
+    assert e(ODD, 4, 64, 64, None, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_ALIGN
+    assert e(A16, 4, 64, 64, A16 + 1, A16, A16, A16, A16, A16, None) == kq.KQ_ERR_ALIGN
+    assert e(A16, 4, 64, 64, None, A16, A16, A16, A16, A16, A16 + 2) == kq.KQ_ERR_ALIGN
+    r = kq.kq_calib_es_run
+    assert r(A16, 4, 64, 64, None, A16, A16, A16, A16, A16, -1, None) == kq.KQ_ERR_SHAPE
+    assert r(A16, 4, 64, 64, None, A16, A16, A16, A16, A16, 1 << 25, None) == kq.KQ_ERR_SHAPE
+    assert r(A16, 4, 64, 64, None, None, None, None, None, None, 0, None) == kq.KQ_OK
+    assert r(A16, 4, 64, 64, None, A16, A16, A16, None, A16, 3, None) == kq.KQ_ERR_NULL
+    assert r(A16, 4, 64, 64, None, A16, A16, A16, A16, A16 + 1, 3, None) == kq.KQ_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -89,6 +89,109 @@ def test_es_update_bit_exact(torch_cuda):
         np.testing.assert_array_equal(_np(got).view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("with_gram,strided", [(False, False), (True, True)])
+def test_es_step_equals_objective_then_update(torch_cuda, with_gram, strided):
+    """kq_calib_es_step is defined as kq_calib_objective on the candidates
+    followed by kq_calib_es_update: run both sequences side by side for several
+    iterations and compare every state array bit for bit after each one."""
+    torch = torch_cuda
+    x = inputs.activation("flux_attn")[:300]
+    nb = 64 if strided else 96
+    d = nb * 32
+    xd = to_gpu_bf16(x)
+    gram = None
+    if with_gram:
+        g = np.random.default_rng(11)
+        w = g.normal(0, 1, (nb, 48, 32))
+        gram = to_gpu(np.einsum("jab,jac->jbc", w, w).astype(np.float32) / 48)
+    noise = to_gpu(inputs.calib_noise("flux_attn", 6, blocks=nb))
+    start = inputs.hadamard_init(nb).reshape(nb, 15)
+    st = torch.cuda.current_stream().cuda_stream
+    gp = gram.data_ptr() if gram is not None else None
+
+    def fresh():
+        theta = to_gpu(start.copy())
+        sigma = torch.full((nb,), 0.05, dtype=torch.float32, device="cuda")
+        fbest = kq.calib_objective(xd, theta, gram, d=d)
+        cand = theta.clone()
+        inf = torch.full((nb,), float("inf"), dtype=torch.float32, device="cuda")
+        assert kq.kq_calib_es_update(nb, theta.data_ptr(), sigma.data_ptr(), fbest.data_ptr(),
+                                     cand.data_ptr(), inf.data_ptr(), noise[0].data_ptr(),
+                                     st) == kq.KQ_OK
+        return theta, sigma, fbest, cand
+
+    a, b = fresh(), fresh()
+    fcand = torch.empty(nb, dtype=torch.float32, device="cuda")
+    fhist = torch.full((nb,), -1.0, dtype=torch.float32, device="cuda")
+    for i in range(1, noise.shape[0]):
+        kq.calib_objective(xd, a[3], gram, d=d, f=fcand)
+        assert kq.kq_calib_es_update(nb, *[t.data_ptr() for t in a], fcand.data_ptr(),
+                                     noise[i].data_ptr(), st) == kq.KQ_OK
+        assert kq.kq_calib_es_step(xd.data_ptr(), x.shape[0], d, xd.stride(0), gp,
+                                   *[t.data_ptr() for t in b], noise[i].data_ptr(),
+                                   fhist.data_ptr(), st) == kq.KQ_OK
+        for ga, gb in zip(a, b):
+            np.testing.assert_array_equal(_np(ga).view(np.uint32), _np(gb).view(np.uint32))
+        np.testing.assert_array_equal(_np(fhist).view(np.uint32), _np(b[2]).view(np.uint32))
+    # at least one block kept a candidate, so the update path was exercised
+    assert not np.array_equal(_np(b[0]), start)
+    # the kept objective is the objective of the kept parameters
+    np.testing.assert_array_equal(_np(kq.calib_objective(xd, b[0], gram, d=d)), _np(b[2]))
+
+
+def test_es_run_equals_repeated_steps(torch_cuda):
+    """kq_calib_es_run over several iterations against the same number of
+    kq_calib_es_step calls, bit for bit, history rows included."""
+    torch = torch_cuda
+    x = to_gpu_bf16(inputs.activation("pixart")[:200])
+    nb, iters = 36, 7
+    noise = to_gpu(inputs.calib_noise("pixart", iters - 1, blocks=nb))
+    start = inputs.hadamard_init(nb).reshape(nb, 15)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def state():
+        theta = to_gpu(start.copy())
+        cand = to_gpu((start + 0.01).astype(np.float32))
+        sigma = torch.full((nb,), 0.05, dtype=torch.float32, device="cuda")
+        fbest = kq.calib_objective(x, theta)
+        return [theta, sigma, fbest, cand]
+
+    a, b = state(), state()
+    ha = torch.full((iters, nb), -1.0, dtype=torch.float32, device="cuda")
+    hb = torch.full((iters, nb), -1.0, dtype=torch.float32, device="cuda")
+    for i in range(iters):
+        assert kq.kq_calib_es_step(x.data_ptr(), x.shape[0], nb * 32, x.stride(0), None,
+                                   *[t.data_ptr() for t in a], noise[i].data_ptr(),
+                                   ha[i].data_ptr(), st) == kq.KQ_OK
+    assert kq.kq_calib_es_run(x.data_ptr(), x.shape[0], nb * 32, x.stride(0), None,
+                              *[t.data_ptr() for t in b], noise.data_ptr(), iters,
+                              hb.data_ptr(), st) == kq.KQ_OK
+    for ga, gb in zip(a + [ha], b + [hb]):
+        np.testing.assert_array_equal(_np(ga).view(np.uint32), _np(gb).view(np.uint32))
+    assert np.all(_np(hb) >= 0)
+
+
+def test_es_step_with_no_tokens(torch_cuda):
+    torch = torch_cuda
+    nb = 4
+    xd = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    theta = to_gpu(inputs.hadamard_init(nb).reshape(nb, 15))
+    cand = theta.clone()
+    sigma = torch.full((nb,), 0.05, dtype=torch.float32, device="cuda")
+    fbest = torch.zeros(nb, dtype=torch.float32, device="cuda")
+    noise = torch.ones((nb, 15), dtype=torch.float32, device="cuda")
+    assert kq.kq_calib_es_step(xd.data_ptr(), 0, 128, 128, None, theta.data_ptr(),
+                               sigma.data_ptr(), fbest.data_ptr(), cand.data_ptr(),
+                               noise.data_ptr(), None,
+                               torch.cuda.current_stream().cuda_stream) == kq.KQ_OK
+    # objective 0 is not below the kept 0: rejected, sigma shrinks, next candidate proposed
+    np.testing.assert_array_equal(_np(theta), inputs.hadamard_init(nb).reshape(nb, 15))
+    np.testing.assert_array_equal(_np(sigma), np.full(nb, np.float32(0.05) * np.float32(0.90360200)))
+    assert np.all(_np(fbest) == 0)
+    want = (np.float32(0.05) * np.float32(0.90360200)) + inputs.hadamard_init(nb).reshape(nb, 15)
+    np.testing.assert_array_equal(_np(cand), want)
+
+
 def test_calibration_lowers_held_out_error(torch_cuda):
     torch = torch_cuda
     x = inputs.activation("flux_attn")
