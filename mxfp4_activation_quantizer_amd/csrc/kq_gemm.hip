@@ -49,6 +49,12 @@
 // Epilogue: the bf16 tile is written into two of the (then free) stages, in
 // an XOR slot layout that keeps the 32-row accumulator stores conflict-free,
 // and every wave stores two whole 512-byte tile rows per instruction.
+//
+// All of the above describes the per-tile kernel, which takes any K that is
+// a multiple of 128.  A K that is a multiple of 1536 takes the pipelined
+// kernel further down: the same tiles, MFMAs and epilogue, with the K
+// pipeline carried across output tiles and the scales in a ring of their
+// own.
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -419,17 +425,120 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined form for K a multiple of three K tiles (K % 768 == 0): every
-// output tile then starts at stage 0, K tile k of any tile sits in stage
-// k % 3, and the pipeline runs on across output tiles.  The last two steps
-// of a tile issue the next tile's first two K tiles, and the epilogue runs
-// in stage 2 (its last K tile's, free once multiplied) while those are in
+// Pipelined form for K a multiple of six K tiles (K % 1536 == 0): every
+// output tile starts at stage 0, K tile k of any tile sits in stage k % 3,
+// and the pipeline runs on across output tiles.  The last two steps of a
+// tile issue the next tile's first two K tiles, and the epilogue runs in
+// stage 2 (its last K tile's, free once multiplied) while those are in
 // flight: no pipeline fill per tile and no idle epilogue.
-// Waits per step as above: vmcnt(one tile's DMAs) then a barrier.  At a
+//
+// Scales travel apart from the codes.  One row's scale bytes for two
+// consecutive K tiles are 16 contiguous bytes, so with every even K tile one
+// 16-byte DMA per wave (48 active lanes, one row each) brings the 384 rows
+// of both operands for that pair into one slot of a two-slot ring: 8 wave
+// instructions per two K tiles where per-tile 4-byte DMAs took 32, each of
+// those touching 32 cache lines for 256 bytes.  Pair n of the workgroup's
+// running sequence sits in slot n % 2; it is fetched with its first K tile,
+// two steps before it is read, after the barrier that ends the reads of
+// pair n - 2 in that slot.
+//
+// This kernel issues its DMAs through inline assembly, so the compiler
+// neither sees them nor adds waits for them (it cannot tell the ring slots
+// apart and would drain at every read).  The waits are explicit: before K
+// tile s is read, vmcnt(the DMAs of the step before) retires it; a step
+// issues six code DMAs, plus the scale DMA when its K tile is even.  At a
 // tile's first two steps the outstanding operations also include the
-// previous epilogue's stores, which are younger than the K tile waited
-// for, so the same count still retires it.
+// previous epilogue's stores, which are younger than the K tile waited for,
+// so the same count still retires it.
 // ---------------------------------------------------------------------------
+constexpr int kPStage = kAB + kWB;                               // codes of one K tile: 49152
+constexpr int kRingRows = kBM + kBN;                             // A rows, then W rows
+constexpr int kRingSlot = 16 * kRingRows;                        // 6144
+constexpr int kRingRowsPerWave = kRingRows / (kGemmThreads / 64);  // 48
+constexpr int kPipeK = 6 * kBK;                                  // K granule of this kernel
+static_assert(kRingRows % (kGemmThreads / 64) == 0 && kRingRowsPerWave <= 64, "one scale DMA per wave");
+static_assert(3 * kPStage + 2 * kRingSlot <= 160 * 1024, "LDS of the pipelined kernel");
+static_assert(kDA + kDW == 6, "six code DMAs per step");
+
+__shared__ __attribute__((aligned(16))) uint8_t gp_st0[kPStage];
+__shared__ __attribute__((aligned(16))) uint8_t gp_st1[kPStage];
+__shared__ __attribute__((aligned(16))) uint8_t gp_st2[kPStage];
+__shared__ __attribute__((aligned(16))) uint8_t gp_ring[2 * kRingSlot];
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t *l) {
+    return (uint32_t)(uintptr_t)(lds_void *)l;
+}
+// A 16-byte LDS DMA the compiler does not track.  M0 holds the LDS base
+// (lane l writes at M0 + 16 l); one wait state must separate the write of
+// M0 from the DMA that reads it.
+__device__ __forceinline__ void dma16_raw(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+struct PipePlan {
+    int ga[kDA], gw[kDW];   // code offsets at K tile 0, as in DmaPlan
+    const uint8_t *sp;      // this lane's scale row (lanes < kRingRowsPerWave)
+};
+
+__device__ __forceinline__ void make_pipe_plan(PipePlan &pl, int m0, int n0, int M, int N, int K2,
+                                               int K32, int wave, int lane, const uint8_t *as,
+                                               const uint8_t *ws) {
+#pragma unroll
+    for (int q = 0; q < kDA; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < kDW; ++q) {
+        const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
+        const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
+    }
+    const int r = wave * kRingRowsPerWave + (lane < kRingRowsPerWave ? lane : 0);
+    pl.sp = r < kBM ? as + (int64_t)(m0 + r < M ? m0 + r : M - 1) * K32
+                    : ws + (int64_t)(n0 + r - kBM < N ? n0 + r - kBM : N - 1) * K32;
+}
+
+// K tile kt of both operands into stage st; with an even kt also the scale
+// pair kt / 2 into ring slot `slot`.
+__device__ __forceinline__ void pipe_issue(const PipePlan &pl, const uint8_t *ac, const uint8_t *wc,
+                                           int kt, int wave, int lane, const uint8_t *st, int slot) {
+    if ((kt & 1) == 0 && lane < kRingRowsPerWave)
+        dma16_raw(pl.sp + 8 * kt, lds_u32(gp_ring + slot * kRingSlot + wave * kRingRowsPerWave * 16));
+#pragma unroll
+    for (int q = 0; q < kDA; ++q)
+        dma16_raw(ac + pl.ga[q] + kt * kRowBytes, lds_u32(st + (q * (kGemmThreads / 64) + wave) * 1024));
+#pragma unroll
+    for (int q = 0; q < kDW; ++q)
+        dma16_raw(wc + pl.gw[q] + kt * kRowBytes,
+                  lds_u32(st + kAB + (q * (kGemmThreads / 64) + wave) * 1024));
+}
+
+// One K tile from stage b with its scales at rs (the ring slot plus 8 bytes
+// for an odd K tile): each row's 8-byte word, shifted one byte for the upper
+// 32 K values of a step, as in gemm_compute.
+__device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, const uint8_t *rs, int wm,
+                                             int wn, int i32, int kg, f32x16g (&acc)[2][2]) {
+    u32x2g sa[2], sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(rs + (wm * 64 + j * 32 + i32) * 16) >> (8 * kg);
+        sa[j] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint64_t v =
+            *reinterpret_cast<const uint64_t *>(rs + (kBM + wn * 64 + i * 32 + i32) * 16) >> (8 * kg);
+        sw[i] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+    }
+    gemm_kstep<0>(b, wm, wn, i32, kg, sa, sw, acc);
+    gemm_kstep<1>(b, wm, wn, i32, kg, sa, sw, acc);
+    gemm_kstep<2>(b, wm, wn, i32, kg, sa, sw, acc);
+    gemm_kstep<3>(b, wm, wn, i32, kg, sa, sw, acc);
+}
+
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
@@ -444,14 +553,16 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     const int wm = wave / kGemmWN, wn = wave % kGemmWN;
     const int i32 = lane & 31, kg = lane >> 5;
     const int K2 = K / 2, K32 = K / 32;
-    const int KT = K / kBK;  // a multiple of 3, no half tile
+    const int KT = K / kBK;              // a multiple of 6
+    const int flip = (KT / 2) & 1;       // ring slot change from one tile's pair 0 to the next's
 
     int m0, n0;
     tile_origin(xcd * per + t, mtc, ntc, m0, n0);
-    DmaPlan pc;
-    make_plan(pc, m0, n0, M, N, K2, K32, wave, lane, as, ws);
-    gemm_issue(pc, ac, wc, 0, false, wave, gemm_st0);
-    gemm_issue(pc, ac, wc, 1, false, wave, gemm_st1);
+    PipePlan pc;
+    make_pipe_plan(pc, m0, n0, M, N, K2, K32, wave, lane, as, ws);
+    int pb = 0;                          // ring slot of this tile's scale pair 0
+    pipe_issue(pc, ac, wc, 0, wave, lane, gp_st0, pb);
+    pipe_issue(pc, ac, wc, 1, wave, lane, gp_st1, pb);
 
     f32x16g acc[2][2];
     auto barrier = [] { __builtin_amdgcn_s_barrier(); };
@@ -462,8 +573,9 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
         const bool has_next = tn < per && xcd * per + tn < tiles;
         int m1 = m0, n1 = n0;
         if (has_next) tile_origin(xcd * per + tn, mtc, ntc, m1, n1);
-        DmaPlan pn;
-        make_plan(pn, m1, n1, M, N, K2, K32, wave, lane, as, ws);
+        PipePlan pn;
+        make_pipe_plan(pn, m1, n1, M, N, K2, K32, wave, lane, as, ws);
+        const int pbn = pb ^ flip;
 
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -471,33 +583,40 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
 
         // step s: retire K tile s, issue K tile s + 2 (or the next tile's
-        // s + 2 - KT) into stage (s + 2) % 3, multiply K tile s from stage s % 3
-        constexpr int kSteps = 15;
+        // s + 2 - KT) into stage (s + 2) % 3, multiply K tile s from stage
+        // s % 3.  Twelve steps per pass keep both the stage (s % 3) and the
+        // parity of s fixed for each unrolled step.
+        constexpr int kSteps = 12;
         for (int s0 = 0; s0 < KT; s0 += kSteps) {
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
                 const int st = s0 + u;
                 if (st >= KT) break;
-                uint8_t *in = u % 3 == 1 ? gemm_st0 : u % 3 == 2 ? gemm_st1 : gemm_st2;
-                const uint8_t *rd = u % 3 == 0 ? gemm_st0 : u % 3 == 1 ? gemm_st1 : gemm_st2;
-                KQ_WAIT_VM(kDPerTile);
+                const uint8_t *in = u % 3 == 1 ? gp_st0 : u % 3 == 2 ? gp_st1 : gp_st2;
+                const uint8_t *rd = u % 3 == 0 ? gp_st0 : u % 3 == 1 ? gp_st1 : gp_st2;
+                // the step before issued 6 DMAs, 7 when its K tile (s + 1) was even
+                if (u & 1) KQ_WAIT_VM(kDA + kDW + 1);
+                else KQ_WAIT_VM(kDA + kDW);
                 __builtin_amdgcn_s_barrier();
-                if (st + 2 < KT) gemm_issue(pc, ac, wc, st + 2, false, wave, in);
-                else gemm_issue(pn, ac, wc, st + 2 - KT, false, wave, in);
-                gemm_compute(rd, kBK / 64, wm, wn, i32, kg, acc);
+                const int f = st + 2;
+                if (f < KT) pipe_issue(pc, ac, wc, f, wave, lane, in, (pb + (f >> 1)) & 1);
+                else pipe_issue(pn, ac, wc, f - KT, wave, lane, in, (pbn + ((f - KT) >> 1)) & 1);
+                pipe_compute(rd, gp_ring + ((pb + (st >> 1)) & 1) * kRingSlot + 8 * (u & 1), wm, wn,
+                             i32, kg, acc);
             }
         }
         // epilogue in stage 2 (K tile KT - 1's, KT a multiple of 3), two
         // passes of 64 rows; stages 0 and 1 take the next tile's first K tiles
         __builtin_amdgcn_s_barrier();
-        store_rows64(acc, 0, gemm_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_rows64(acc, 0, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         __builtin_amdgcn_s_barrier();
-        store_rows64(acc, 64, gemm_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_rows64(acc, 64, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         if (!has_next) break;
         t = tn;
         m0 = m1;
         n0 = n1;
         pc = pn;
+        pb = pbn;
     }
     // the last repeats may still be landing in LDS: finish before the
     // workgroup's LDS is handed to another
@@ -529,7 +648,7 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
     static const int pipe_env = env_override("KQ_GEMM_PIPE", 1, [](int v) { return v == 0 || v == 1; });
-    const bool pipe = pipe_env && K % (3 * kBK) == 0;
+    const bool pipe = pipe_env && K % kPipeK == 0;
     const void *fn = pipe ? (const void *)w4a4_gemm_pipe_kernel : (const void *)w4a4_gemm_kernel;
     // The explicit vmcnt waits count this kernel's DMAs; register spills would
     // add scratch loads and stores to that count and let a stage be read

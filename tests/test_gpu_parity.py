@@ -600,10 +600,14 @@ def _random_mxfp4(g, rows, k, lo=118, hi=128):
                                    # K past one 15-step pass of the K pipeline
                                    # (3328), whole and ending in a half tile
                                    (70, 260, 4096), (33, 40, 4224), (5, 8, 7808),
-                                   # K a multiple of 768: the cross-tile
-                                   # pipelined kernel (6912: two loop passes)
-                                   (130, 300, 768), (257, 513, 1536), (5, 17, 2304),
-                                   (64, 256, 6912)])
+                                   # K a multiple of 768 but not of 1536:
+                                   # the per-tile kernel
+                                   (130, 300, 768), (5, 17, 2304), (64, 256, 6912),
+                                   # K a multiple of 1536: the cross-tile
+                                   # pipelined kernel (1536: an odd number of
+                                   # scale pairs per tile; 4608 and 9216: two
+                                   # and three passes of its 12-step loop)
+                                   (257, 513, 1536), (70, 260, 4608), (33, 520, 9216)])
 def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     torch = torch_cuda
     g = np.random.default_rng(M * 7 + N * 3 + K)
@@ -616,7 +620,7 @@ def test_gemm_random_mxfp4(torch_cuda, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8),
-                                       (70, 260, 768, 12)])
+                                       (70, 260, 768, 12), (70, 260, 1536, 12)])
 def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     """Row stride beyond N: the whole-row epilogue writes only columns < N
     of rows < M; the padding keeps its sentinel."""
@@ -633,14 +637,17 @@ def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     assert (inputs.bf16_bits_to_f32(yb[:, N:]) == 5.0).all()
 
 
-def test_gemm_workgroups_walk_several_tiles(torch_cuda):
+@pytest.mark.parametrize("K", [768, 1536, 3072])
+def test_gemm_workgroups_walk_several_tiles(torch_cuda, K):
     """More output tiles (20 x 16 = 320) than workgroups (one per CU): the
-    persistent workgroups carry the K pipeline from one tile into the next
-    (K = 768, the pipelined kernel).  Three rows of every M tile are checked
-    over all N columns."""
+    persistent workgroups walk several tiles.  K = 768 takes the per-tile
+    kernel; 1536 and 3072 the pipelined one, which carries the K pipeline and
+    the scale ring from one tile into the next (1536: three scale pairs per
+    tile, so the ring slot of a tile's first pair alternates; 3072: six).
+    Three rows of every M tile are checked over all N columns."""
     torch = torch_cuda
-    M, N, K = 2560, 4096, 768
-    g = np.random.default_rng(77)
+    M, N = 2560, 4096
+    g = np.random.default_rng(77 + K)
     ac, as_ = _random_mxfp4(g, M, K)
     wc, ws = _random_mxfp4(g, N, K)
     y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
