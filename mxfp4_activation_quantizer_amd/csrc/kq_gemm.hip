@@ -518,9 +518,15 @@ __device__ __forceinline__ void pipe_issue(const PipePlan &pl, const uint8_t *ac
 
 // One K tile from stage b with its scales at rs (the ring slot plus 8 bytes
 // for an odd K tile): each row's 8-byte word, shifted one byte for the upper
-// 32 K values of a step, as in gemm_compute.
+// 32 K values of a step, as in gemm_compute.  The step's DMAs (issue) go out
+// after the second of the four K steps: issued right after the barrier, every
+// wave first queues its DMAs and only then starts multiplying; issued half a
+// step later they still have a step and a half to land, and the MFMAs of the
+// first two K steps run meanwhile (2-3% faster than either end of the step).
+template <class Issue>
 __device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, const uint8_t *rs, int wm,
-                                             int wn, int i32, int kg, f32x16g (&acc)[2][2]) {
+                                             int wn, int i32, int kg, f32x16g (&acc)[2][2],
+                                             Issue issue) {
     u32x2g sa[2], sw[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -535,6 +541,7 @@ __device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, cons
     }
     gemm_kstep<0>(b, wm, wn, i32, kg, sa, sw, acc);
     gemm_kstep<1>(b, wm, wn, i32, kg, sa, sw, acc);
+    issue();
     gemm_kstep<2>(b, wm, wn, i32, kg, sa, sw, acc);
     gemm_kstep<3>(b, wm, wn, i32, kg, sa, sw, acc);
 }
@@ -582,10 +589,10 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
 
-        // step s: retire K tile s, issue K tile s + 2 (or the next tile's
-        // s + 2 - KT) into stage (s + 2) % 3, multiply K tile s from stage
-        // s % 3.  Twelve steps per pass keep both the stage (s % 3) and the
-        // parity of s fixed for each unrolled step.
+        // step s: retire K tile s, multiply K tile s from stage s % 3 and,
+        // halfway through, issue K tile s + 2 (or the next tile's s + 2 - KT)
+        // into stage (s + 2) % 3.  Twelve steps per pass keep both the stage
+        // (s % 3) and the parity of s fixed for each unrolled step.
         constexpr int kSteps = 12;
         for (int s0 = 0; s0 < KT; s0 += kSteps) {
 #pragma unroll
@@ -599,10 +606,12 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
                 else KQ_WAIT_VM(kDA + kDW);
                 __builtin_amdgcn_s_barrier();
                 const int f = st + 2;
-                if (f < KT) pipe_issue(pc, ac, wc, f, wave, lane, in, (pb + (f >> 1)) & 1);
-                else pipe_issue(pn, ac, wc, f - KT, wave, lane, in, (pbn + ((f - KT) >> 1)) & 1);
                 pipe_compute(rd, gp_ring + ((pb + (st >> 1)) & 1) * kRingSlot + 8 * (u & 1), wm, wn,
-                             i32, kg, acc);
+                             i32, kg, acc, [&] {
+                                 if (f < KT) pipe_issue(pc, ac, wc, f, wave, lane, in, (pb + (f >> 1)) & 1);
+                                 else pipe_issue(pn, ac, wc, f - KT, wave, lane, in,
+                                                 (pbn + ((f - KT) >> 1)) & 1);
+                             });
             }
         }
         // epilogue in stage 2 (K tile KT - 1's, KT a multiple of 3), two
