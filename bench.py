@@ -90,6 +90,7 @@ rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o copy_FE
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration --steps 20
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ -o SQ -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_mfma -o SQ_mfma -- python3 bench.py --kernel-only --kernel kq_transform_quant_mfma --steps 20 --warmup 5
+rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_gemm -o SQ_gemm -- python3 bench.py --kernel-only --kernel kq_w4a4_gemm --steps 20 --warmup 5
 python3 bench.py --summarize-profiles OUT"""
 
 
@@ -273,7 +274,8 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
            f"{w.tokens}x{w.d}, from rocprofv3 --pmc",
            f"# kernel sources {src_hash}; commands:"]
     ctr += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
-    for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma")):
+    for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma"),
+                       ("SQ_gemm", "kq_w4a4_gemm")):
         if not os.path.isdir(os.path.join(out_dir, sub)):
             ctr.append(f"{entry}: no {sub} pass in {out_dir}")
             continue
@@ -286,9 +288,14 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
         ctr.append(f"{entry}:")
         for k in sorted(means):
             ctr.append(f"  {k:26s} {means[k]:14.1f}")
-        if means.get("SQ_WAVES"):
+        if means.get("SQ_WAVES") and entry != "kq_w4a4_gemm":
             ctr.append(f"  VALU instructions per wave {means['SQ_INSTS_VALU'] / means['SQ_WAVES']:14.1f}")
             ctr.append(f"  VALU lane-ops per element  {64 * means['SQ_INSTS_VALU'] / w.elements:14.2f}")
+        if means.get("SQ_INSTS_MFMA"):
+            ctr.append(f"  MFMA busy cycles per MFMA  {means['SQ_VALU_MFMA_BUSY_CYCLES'] / means['SQ_INSTS_MFMA']:14.1f}")
+        if entry == "kq_w4a4_gemm" and means.get("SQ_INSTS_MFMA"):
+            ctr.append(f"  (one GEMM, {w.tokens}x{inputs.GEMM_N}x{inputs.GEMM_K}: "
+                       f"{2 * w.tokens * inputs.GEMM_N * inputs.GEMM_K / means['SQ_INSTS_MFMA']:.0f} flops per MFMA instruction)")
     with open(os.path.join(PROFILES, f"counters_{workload}.txt"), "w") as f:
         f.write("\n".join(ctr) + "\n")
     print("\n".join(lines + txt + ctr))

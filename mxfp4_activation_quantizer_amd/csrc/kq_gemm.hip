@@ -516,28 +516,39 @@ __device__ __forceinline__ void pipe_issue(const PipePlan &pl, const uint8_t *ac
                   lds_u32(st + kAB + (q * (kGemmThreads / 64) + wave) * 1024));
 }
 
-// One K tile from stage b with its scales at rs (the ring slot plus 8 bytes
-// for an odd K tile): each row's 8-byte word, shifted one byte for the upper
-// 32 K values of a step, as in gemm_compute.  The step's DMAs (issue) go out
-// after the second of the four K steps: issued right after the barrier, every
-// wave first queues its DMAs and only then starts multiplying; issued half a
-// step later they still have a step and a half to land, and the MFMAs of the
-// first two K steps run meanwhile (2-3% faster than either end of the step).
+// The 16 scale bytes (two K tiles) of this lane's four rows (A rows j = 0, 1,
+// then W rows i = 0, 1) from ring slot rs.  One 16-byte read per row and
+// pair: sixteen lanes read sixteen consecutive rows, 256 contiguous bytes,
+// where 8-byte reads of one half of each 16-byte slot would pair rows 16
+// apart on the same banks.
+__device__ __forceinline__ void pipe_scales(const uint8_t *rs, int wm, int wn, int i32, u32x4 (&sc)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        sc[j] = *reinterpret_cast<const u32x4 *>(rs + (wm * 64 + j * 32 + i32) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        sc[2 + i] = *reinterpret_cast<const u32x4 *>(rs + (kBM + wn * 64 + i * 32 + i32) * 16);
+}
+
+// One K tile from stage b; its scale word per row is half `odd` of the
+// row's pair in sc, shifted one byte for the upper 32 K values of a step, as
+// in gemm_compute.  The step's DMAs (issue) go out after the second of the
+// four K steps: issued right after the barrier, every wave first queues its
+// DMAs and only then starts multiplying; issued half a step later they still
+// have a step and a half to land, and the MFMAs of the first two K steps run
+// meanwhile (2-3% faster than either end of the step).
 template <class Issue>
-__device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, const uint8_t *rs, int wm,
-                                             int wn, int i32, int kg, f32x16g (&acc)[2][2],
+__device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, const u32x4 (&sc)[4], int odd,
+                                             int wm, int wn, int i32, int kg, f32x16g (&acc)[2][2],
                                              Issue issue) {
     u32x2g sa[2], sw[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint64_t v = *reinterpret_cast<const uint64_t *>(rs + (wm * 64 + j * 32 + i32) * 16) >> (8 * kg);
-        sa[j] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint64_t v =
-            *reinterpret_cast<const uint64_t *>(rs + (kBM + wn * 64 + i * 32 + i32) * 16) >> (8 * kg);
-        sw[i] = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t w = odd ? ((uint64_t)sc[r][3] << 32 | sc[r][2]) : ((uint64_t)sc[r][1] << 32 | sc[r][0]);
+        const uint64_t v = w >> (8 * kg);
+        const u32x2g x = u32x2g{(uint32_t)v, (uint32_t)(v >> 32)};
+        if (r < 2) sa[r] = x;
+        else sw[r - 2] = x;
     }
     gemm_kstep<0>(b, wm, wn, i32, kg, sa, sw, acc);
     gemm_kstep<1>(b, wm, wn, i32, kg, sa, sw, acc);
@@ -572,6 +583,7 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     pipe_issue(pc, ac, wc, 1, wave, lane, gp_st1, pb);
 
     f32x16g acc[2][2];
+    u32x4 sc[4];  // scale words of the current pair, rows A j = 0, 1 and W i = 0, 1
     auto barrier = [] { __builtin_amdgcn_s_barrier(); };
     for (;;) {
         // the next tile of this workgroup, if any (else the DMAs of the last
@@ -606,8 +618,10 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
                 else KQ_WAIT_VM(kDA + kDW);
                 __builtin_amdgcn_s_barrier();
                 const int f = st + 2;
-                pipe_compute(rd, gp_ring + ((pb + (st >> 1)) & 1) * kRingSlot + 8 * (u & 1), wm, wn,
-                             i32, kg, acc, [&] {
+                // a pair's scale words are read at its first K tile, after
+                // the barrier that follows its arrival, and kept for the second
+                if ((u & 1) == 0) pipe_scales(gp_ring + ((pb + (st >> 1)) & 1) * kRingSlot, wm, wn, i32, sc);
+                pipe_compute(rd, sc, u & 1, wm, wn, i32, kg, acc, [&] {
                                  if (f < KT) pipe_issue(pc, ac, wc, f, wave, lane, in, (pb + (f >> 1)) & 1);
                                  else pipe_issue(pn, ac, wc, f - KT, wave, lane, in,
                                                  (pbn + ((f - KT) >> 1)) & 1);
