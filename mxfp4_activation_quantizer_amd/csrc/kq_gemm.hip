@@ -231,33 +231,29 @@ __device__ __forceinline__ void make_plan(DmaPlan &pl, int m0, int n0, int M, in
     }
 }
 
-// Output rows [r0, r0 + 64) of the tile at (m0, n0), bf16 (nearest even),
-// through LDS buffer ob (64 rows x 512 bytes): the waves holding those rows
-// write them in the 8-byte slot layout (c / 4) ^ (r & 31), then every thread
-// stores 16 bytes, two whole rows per wave instruction.  The caller places
-// a barrier between the write and the read phase (barrier_mid) and after the
-// reads before ob is reused.
+// Half j of the output tile at (m0, n0): rows wm * 64 + j * 32 + (0..31) of
+// both row blocks wm = 0, 1 (64 rows), bf16 (nearest even), through LDS
+// buffer ob (64 rows x 512 bytes).  Every wave writes its 32 rows of the
+// half (LDS row wm * 32 + r) in the 8-byte slot layout (c / 4) ^ (r & 31),
+// so all eight waves share the write phase; then every thread stores 16
+// bytes, two whole rows per wave instruction.  The caller places a barrier
+// between the write and the read phase (barrier_mid) and after the reads
+// before ob is reused.
 template <class Barrier>
-__device__ __forceinline__ void store_rows64(const f32x16g (&acc)[2][2], int r0, uint8_t *ob,
-                                             int wm, int wn, int i32, int kg, int tid, int m0,
-                                             int n0, int M, int N, int64_t ldy, uint16_t *y,
-                                             Barrier barrier_mid) {
-    if (wm * 64 == r0) {
+__device__ __forceinline__ void store_half(const f32x16g (&acc)[2][2], int j, uint8_t *ob, int wm,
+                                           int wn, int i32, int kg, int tid, int m0, int n0, int M,
+                                           int N, int64_t ldy, uint16_t *y, Barrier barrier_mid) {
+    const int lr = wm * 32 + i32;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int lr = j * 32 + i32;
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int s8 = wn * 16 + i * 8 + 2 * q + kg;
-                    const uint32_t lo = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
-                    const uint32_t hi = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
-                    *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
-                }
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int s8 = wn * 16 + i * 8 + 2 * q + kg;
+            const uint32_t lo = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2));
+            const uint32_t hi = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2));
+            *reinterpret_cast<u32x2g *>(ob + lr * (kBN * 2) + 8 * (s8 ^ i32)) = u32x2g{lo, hi};
         }
     }
     barrier_mid();
@@ -268,7 +264,7 @@ __device__ __forceinline__ void store_rows64(const f32x16g (&acc)[2][2], int r0,
         const int row = f / kRowChunks, ch = f % kRowChunks, g = row & 31;
         u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * (kBN * 2) + 16 * (ch ^ (g >> 1)));
         if (g & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int gr = m0 + r0 + row, col = n0 + 8 * ch;
+        const int gr = m0 + (row >> 5) * 64 + j * 32 + g, col = n0 + 8 * ch;
         if (gr >= M || col >= N) continue;
         uint16_t *yp = y + (int64_t)gr * ldy + col;
         if (col + 7 < N) {
@@ -629,11 +625,12 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
             }
         }
         // epilogue in stage 2 (K tile KT - 1's, KT a multiple of 3), two
-        // passes of 64 rows; stages 0 and 1 take the next tile's first K tiles
+        // passes of 64 rows (j = 0: rows 0-31 and 64-95, j = 1: the others);
+        // stages 0 and 1 take the next tile's first K tiles
         __builtin_amdgcn_s_barrier();
-        store_rows64(acc, 0, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_half(acc, 0, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         __builtin_amdgcn_s_barrier();
-        store_rows64(acc, 64, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_half(acc, 1, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         if (!has_next) break;
         t = tn;
         m0 = m1;
