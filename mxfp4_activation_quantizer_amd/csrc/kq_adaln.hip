@@ -38,13 +38,6 @@
 
 namespace kq {
 
-// LDS position (in 16-B chunks) of chunk i (0..7) of block j's 32-float
-// slice of a sample vector.  Lane j reads its block's eight chunks with a
-// 128-B stride between lanes; XOR-ing the chunk index with bits 1..3 of j
-// spreads any 16 consecutive lanes over all 64 banks (no conflicts), and the
-// staging writes, eight consecutive chunks per block, stay conflict-free.
-__device__ __forceinline__ int vec_chunk(int j, int i) { return j * 8 + (i ^ ((j >> 1) & 7)); }
-
 constexpr int kAdalnMaxD = 8192;  // the modulation vectors of one sample live in LDS
                                   // (and d/32 <= 256 fits one 512-thread workgroup)
 

@@ -44,6 +44,14 @@ __device__ __forceinline__ float block_amax(const float (&y)[32]) {
 // exponent 1..252) one fused correction of the hardware estimate,
 // r + r*(1 - u*r), equals IEEE 1/u bit for bit (checked exhaustively over all
 // fp32 inputs on gfx950); any other u takes the IEEE division.
+// LDS position (in 16-B chunks) of chunk i (0..7) of block j's 32-float
+// slice of a per-channel vector staged in LDS.  Lane j reads its block's
+// eight chunks with a 128-B stride between lanes; XOR-ing the chunk index
+// with bits 1..3 of j spreads any 16 consecutive lanes over all 64 banks (no
+// conflicts), and staging writes of eight consecutive chunks per block stay
+// conflict-free.
+__device__ __forceinline__ int vec_chunk(int j, int i) { return j * 8 + (i ^ ((j >> 1) & 7)); }
+
 __device__ __forceinline__ float rcp_rn(float u) {
     const uint32_t ex = (__float_as_uint(u) >> 23) & 0xffu;
     if (__builtin_expect(ex - 1u < 252u, 1)) {

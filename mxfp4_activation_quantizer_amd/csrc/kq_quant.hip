@@ -19,6 +19,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "kq.h"
@@ -122,20 +124,45 @@ struct KronWeightStage : KronInvConsts {
     }
 };
 
-// Per-channel scaling baseline: y_c = x_c * mult_c.
+// Per-channel scaling baseline: y_c = x_c * mult_c.  Lane l of a workgroup
+// takes block (g0 + l) % nb, g0 the workgroup's first unit, so the
+// workgroup touches min(nb, 256) blocks whose multipliers form one range of
+// the [d] vector (wrapping at d).  The workgroup loads that range once into
+// LDS, slot s = block (g0 % nb + s) % nb, 16-byte chunk i at vec_chunk(s, i),
+// in whole 16-byte chunks per thread (consecutive threads, consecutive
+// chunks); lane l then reads slot l % nb.  Loaded lane by lane, each of a
+// wave's eight 16-byte multiplier loads touched 64 cache lines.
+extern __shared__ __attribute__((aligned(16))) f32x4 kq_stage_lds[];
+
 struct SmoothStage {
+    static constexpr bool kShared = true;
     const float *mult;  // [d]
+    int nb;
     __device__ __forceinline__ static SmoothStage from(const float *p) {
         SmoothStage s;
         s.mult = p;
         return s;
     }
+    // LDS bytes the workgroup stages for nb blocks
+    static int64_t shared_bytes(int nb) { return (int64_t)(nb < kBlockThreads ? nb : kBlockThreads) * 128; }
+    // every thread of the workgroup, before any of them leaves
+    __device__ __forceinline__ void share(int g0, int nblocks) {
+        nb = nblocks;
+        const int ns = nb < kBlockThreads ? nb : kBlockThreads, j0 = g0 % nb;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(mult);
+        for (int f = threadIdx.x; f < ns * 8; f += kBlockThreads) {
+            const int sl = f >> 3, i = f & 7;
+            const int j = j0 + sl < nb ? j0 + sl : j0 + sl - nb;
+            kq_stage_lds[vec_chunk(sl, i)] = src[(int64_t)j * 8 + i];
+        }
+        __syncthreads();
+    }
     float m[32];
-    __device__ __forceinline__ void fetch(int j) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(mult + (int64_t)j * 32);
+    __device__ __forceinline__ void fetch(int) {
+        const int sl = (int)(threadIdx.x % (unsigned)nb);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const f32x4 v = p[i];
+            const f32x4 v = kq_stage_lds[vec_chunk(sl, i)];
 #pragma unroll
             for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
         }
@@ -146,6 +173,13 @@ struct SmoothStage {
         for (int k = 0; k < 32; ++k) z[k] = z[k] * m[k];
     }
 };
+
+// Stages that stage per-workgroup data in LDS declare kShared = true and
+// provide share() and shared_bytes(); the others need neither.
+template <class S, class = void>
+struct stage_shares : std::false_type {};
+template <class S>
+struct stage_shares<S, std::void_t<decltype(S::kShared)>> : std::bool_constant<S::kShared> {};
 
 // Orthonormal 32-point Walsh-Hadamard (Sylvester order, LRQ-DiT Eq. (3)):
 // five add/subtract stages, then one multiply by fl32(1/sqrt(32)).
@@ -266,6 +300,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const flo
                                                               Sink sink,
                                                               int tokens, int nb, int tstep) {
     Stage stage = Stage::from(stage_param);
+    if constexpr (stage_shares<Stage>::value) stage.share(blockIdx.x * kBlockThreads, nb);
     const int g = blockIdx.x * kBlockThreads + threadIdx.x;
     const int j = g % nb;
     int t0 = g / nb;
@@ -378,10 +413,10 @@ static kq_status check_shape(int64_t tokens, int64_t d, int64_t ld) {
 }
 
 template <class Kernel, class... Args>
-static kq_status launch(Kernel kernel, const Plan &pl, void *stream, Args... args) {
+static kq_status launch(Kernel kernel, const Plan &pl, size_t shmem, void *stream, Args... args) {
     void *argv[] = {(void *)&args...};
     hipError_t e = hipLaunchKernel((const void *)kernel, dim3(pl.grid), dim3(kBlockThreads), argv,
-                                   0, (hipStream_t)stream);
+                                   shmem, (hipStream_t)stream);
     return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
@@ -391,11 +426,13 @@ static kq_status run(const Src &src, const float *stage, const Sink &sink, int64
     Plan pl;
     if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
     const int t = (int)tokens;
+    size_t sh = 0;
+    if constexpr (stage_shares<Stage>::value) sh = (size_t)Stage::shared_bytes(nb);
     switch (pl.nu) {
-        case 1: return launch(block_kernel<Src, Stage, Sink, 1>, pl, stream, src, stage, sink, t, nb, pl.tstep);
-        case 2: return launch(block_kernel<Src, Stage, Sink, 2>, pl, stream, src, stage, sink, t, nb, pl.tstep);
-        case 8: return launch(block_kernel<Src, Stage, Sink, 8>, pl, stream, src, stage, sink, t, nb, pl.tstep);
-        default: return launch(block_kernel<Src, Stage, Sink, 4>, pl, stream, src, stage, sink, t, nb, pl.tstep);
+        case 1: return launch(block_kernel<Src, Stage, Sink, 1>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
+        case 2: return launch(block_kernel<Src, Stage, Sink, 2>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
+        case 8: return launch(block_kernel<Src, Stage, Sink, 8>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
+        default: return launch(block_kernel<Src, Stage, Sink, 4>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
     }
 }
 
