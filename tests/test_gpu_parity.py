@@ -277,6 +277,26 @@ def test_smooth_quant_bit_exact(torch_cuda):
     np.testing.assert_array_equal(_np(c), wc)
 
 
+@pytest.mark.parametrize("tokens,nb,pad", [(1, 1, 0), (77, 3, 8), (300, 96, 0), (5, 255, 16),
+                                           (9, 300, 0), (3, 700, 8)])
+def test_smooth_quant_ragged_shapes_and_strides(torch_cuda, tokens, nb, pad):
+    """Each workgroup stages the multipliers of the blocks its lanes touch
+    (min(nb, 256) blocks, a range of the vector that wraps at d): nb below,
+    at and above 256, wrapping inside a workgroup, ragged token counts and
+    strided rows with NaN padding that must never be read."""
+    torch = torch_cuda
+    g = np.random.default_rng(tokens * 7 + nb)
+    d = nb * 32
+    xf = g.standard_normal((tokens, d + pad)) * np.exp(g.standard_normal((tokens, 1)))
+    x = inputs.f64_to_bf16_bits(xf)
+    x[:, d:] = 0x7FC0
+    m = np.exp(g.normal(0, 1.5, d)).astype(np.float32)
+    c, s = kq.smooth_quant(to_gpu_bf16(x), to_gpu(m), d=d)
+    wc, ws = oracle.smooth_quant(x, m, d=d)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+
+
 def test_fwht32_quant_bit_exact_and_vs_definition(torch_cuda):
     x = inputs.activation("tiny")
     c, s = kq.fwht32_quant(to_gpu_bf16(x))
