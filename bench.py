@@ -178,6 +178,21 @@ def _find(directory, suffix):
     raise FileNotFoundError(f"no *{suffix} under {directory}")
 
 
+def profile_commands(workload: str = "flux_attn") -> list:
+    """PROFILE_COMMANDS for a workload: the bench runs take --workload when it
+    is not the default one (the copy calibration is the same for all)."""
+    from mxfp4_activation_quantizer_amd import inputs
+    gemm = inputs.WORKLOADS[workload].d == inputs.GEMM_K  # the consumer takes K = 3072
+    out = []
+    for c in PROFILE_COMMANDS.splitlines():
+        if not gemm and "kq_w4a4_gemm" in c:
+            continue
+        if workload != "flux_attn" and "bench.py --" in c and "--copy-calibration" not in c:
+            c = c.replace("bench.py --", f"bench.py --workload {workload} --", 1)
+        out.append(c)
+    return out
+
+
 def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
     """Turn the rocprofv3 CSV outputs of PROFILE_COMMANDS into the short
     summaries kept under profiles/ (kernel durations; HBM bytes per launch
@@ -202,7 +217,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
 
     lines = [f"# rocprofv3 --kernel-trace --stats, {workload} {w.tokens}x{w.d} bf16, one MI355X",
              f"# kernel sources {src_hash}; commands (REPO = repository root, OUT = output dir):"]
-    lines += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    lines += ["#   " + c for c in profile_commands(workload)]
     lines.append(f"# algorithmic bytes per launch: {nbytes}")
     lines.append(f"{'entry point':26s} {'calls':>6s} {'avg us':>8s} {'med us':>8s} {'p90 us':>8s} "
                  f"{'min us':>8s} {'max us':>8s} {'GB/s(avg)':>10s}")
@@ -260,7 +275,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
         f.write("\n")
     txt = [f"# HBM traffic of kq_transform_quant, {workload} {w.tokens}x{w.d}, from rocprofv3 --pmc",
            f"# kernel sources {src_hash}; commands:"]
-    txt += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    txt += ["#   " + c for c in profile_commands(workload)]
     txt += [f"FETCH_SIZE per dispatch   {kf:12.1f} KiB (x{fs:.4f} copy scale) = {read_b / 1e6:9.3f} MB",
             f"WRITE_SIZE per dispatch   {kw:12.1f} KiB (x{ws:.4f} copy scale) = {write_b / 1e6:9.3f} MB",
             f"64 MiB device copy reads  FETCH_SIZE {cf:10.1f} KiB, WRITE_SIZE {cw:10.1f} KiB",
@@ -273,7 +288,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
     ctr = [f"# SQ counters per dispatch (mean over the dispatches), {workload} "
            f"{w.tokens}x{w.d}, from rocprofv3 --pmc",
            f"# kernel sources {src_hash}; commands:"]
-    ctr += ["#   " + c for c in PROFILE_COMMANDS.splitlines()]
+    ctr += ["#   " + c for c in profile_commands(workload)]
     for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma"),
                        ("SQ_gemm", "kq_w4a4_gemm")):
         if not os.path.isdir(os.path.join(out_dir, sub)):

@@ -125,17 +125,22 @@ struct KronWeightStage : KronInvConsts {
 };
 
 // Per-channel scaling baseline: y_c = x_c * mult_c.  Lane l of a workgroup
-// takes block (g0 + l) % nb, g0 the workgroup's first unit, so the
-// workgroup touches min(nb, 256) blocks whose multipliers form one range of
-// the [d] vector (wrapping at d).  The workgroup loads that range once into
-// LDS, slot s = block (g0 % nb + s) % nb, 16-byte chunk i at vec_chunk(s, i),
-// in whole 16-byte chunks per thread (consecutive threads, consecutive
-// chunks); lane l then reads slot l % nb.  Loaded lane by lane, each of a
-// wave's eight 16-byte multiplier loads touched 64 cache lines.
+// takes block (g0 + l) % nb, g0 the workgroup's first unit.  With
+// nb <= kSmoothStageMax the workgroup's lanes share their blocks (each block
+// at least twice), so the workgroup loads the nb blocks' multipliers once
+// into LDS, in whole 16-byte chunks (consecutive threads, consecutive
+// chunks), slot s = block (g0 % nb + s) % nb with chunk i at vec_chunk(s, i),
+// and lane l reads slot l % nb.  Loaded lane by lane, each of a wave's eight
+// 16-byte multiplier loads touches 64 cache lines.  With more blocks there is
+// no reuse to win and the staging would only take LDS (and resident waves),
+// so each lane loads its own 128 bytes.
 extern __shared__ __attribute__((aligned(16))) f32x4 kq_stage_lds[];
+
+constexpr int kSmoothStageMax = 128;  // 16 KB of LDS: seven workgroups per CU still fit
 
 struct SmoothStage {
     static constexpr bool kShared = true;
+    static constexpr int kUnitsPerLane = 4;
     const float *mult;  // [d]
     int nb;
     __device__ __forceinline__ static SmoothStage from(const float *p) {
@@ -144,13 +149,14 @@ struct SmoothStage {
         return s;
     }
     // LDS bytes the workgroup stages for nb blocks
-    static int64_t shared_bytes(int nb) { return (int64_t)(nb < kBlockThreads ? nb : kBlockThreads) * 128; }
+    static int64_t shared_bytes(int nb) { return nb <= kSmoothStageMax ? (int64_t)nb * 128 : 0; }
     // every thread of the workgroup, before any of them leaves
     __device__ __forceinline__ void share(int g0, int nblocks) {
         nb = nblocks;
-        const int ns = nb < kBlockThreads ? nb : kBlockThreads, j0 = g0 % nb;
+        if (nb > kSmoothStageMax) return;
+        const int j0 = g0 % nb;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(mult);
-        for (int f = threadIdx.x; f < ns * 8; f += kBlockThreads) {
+        for (int f = threadIdx.x; f < nb * 8; f += kBlockThreads) {
             const int sl = f >> 3, i = f & 7;
             const int j = j0 + sl < nb ? j0 + sl : j0 + sl - nb;
             kq_stage_lds[vec_chunk(sl, i)] = src[(int64_t)j * 8 + i];
@@ -158,13 +164,23 @@ struct SmoothStage {
         __syncthreads();
     }
     float m[32];
-    __device__ __forceinline__ void fetch(int) {
-        const int sl = (int)(threadIdx.x % (unsigned)nb);
+    __device__ __forceinline__ void fetch(int j) {
+        if (nb <= kSmoothStageMax) {
+            const int sl = (int)(threadIdx.x % (unsigned)nb);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f32x4 v = kq_stage_lds[vec_chunk(sl, i)];
+            for (int i = 0; i < 8; ++i) {
+                const f32x4 v = kq_stage_lds[vec_chunk(sl, i)];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
+                for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
+            }
+        } else {
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(mult + (int64_t)j * 32);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const f32x4 v = p[i];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) m[4 * i + c] = v[c];
+            }
         }
     }
     __device__ __forceinline__ void setup() {}
@@ -374,24 +390,34 @@ struct Plan {
     int tstep;  // tokens between consecutive units of a lane
 };
 
-// Units per lane: 1 by default.  More units per lane amortise the per-block
-// constant setup (fewer VALU instructions per unit), but on gfx950 the
-// launch is short enough that the number of resident waves decides: one
-// unit per lane (occupancy 7, every wave resident from the start) measured
-// 3-8 % faster than 2, 4 or 8 units per lane on 4608 x 3072.
-// KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
-static int units_per_lane() {
-    static const int v = env_override("KQ_UNITS_PER_LANE", 1,
+// Units per lane: 1 unless the stage asks for more (kUnitsPerLane).  More
+// units per lane amortise the per-block constant setup (fewer VALU
+// instructions per unit), but on gfx950 the launch is short enough that the
+// number of resident waves decides: for the Kronecker stage one unit per
+// lane (occupancy 7, every wave resident from the start) measured 3-8 %
+// faster than 2, 4 or 8 units per lane on 4608 x 3072.  The scaling stage's
+// 128 bytes of multipliers per block are the other way round: four units per
+// lane reuse them four times (8.7 against 9.0 us on 4608 x 3072, 29.7
+// against 36.5 us on 4608 x 12288).  KQ_UNITS_PER_LANE (1, 2, 4 or 8; read
+// once) overrides both for sweeps.
+template <class S, class = void>
+struct stage_units : std::integral_constant<int, 1> {};
+template <class S>
+struct stage_units<S, std::void_t<decltype(S::kUnitsPerLane)>>
+    : std::integral_constant<int, S::kUnitsPerLane> {};
+
+static int units_per_lane(int stage_default) {
+    static const int v = env_override("KQ_UNITS_PER_LANE", 0,
                                       [](int p) { return p == 1 || p == 2 || p == 4 || p == 8; });
-    return v;
+    return v ? v : stage_default;
 }
 
-static bool plan_launch(int64_t tokens, int nb, Plan &pl) {
+static bool plan_launch(int64_t tokens, int nb, int nu, Plan &pl) {
     // The lane count must be a multiple of nb (so a lane keeps one block):
     // the grid is a multiple of m = nb / gcd(nb, threads per workgroup).
     const int64_t m = nb / gcd_int(nb, kBlockThreads);
     const int64_t units = tokens * nb;
-    pl.nu = units_per_lane();
+    pl.nu = nu;
     const int64_t per_wg = (int64_t)kBlockThreads * pl.nu;
     int64_t grid = (units + per_wg - 1) / per_wg;
     grid = (grid + m - 1) / m * m;
@@ -424,7 +450,7 @@ template <class Src, class Stage, class Sink>
 static kq_status run(const Src &src, const float *stage, const Sink &sink, int64_t tokens, int nb,
                      void *stream) {
     Plan pl;
-    if (!plan_launch(tokens, nb, pl)) return KQ_ERR_SHAPE;
+    if (!plan_launch(tokens, nb, units_per_lane(stage_units<Stage>::value), pl)) return KQ_ERR_SHAPE;
     const int t = (int)tokens;
     size_t sh = 0;
     if constexpr (stage_shares<Stage>::value) sh = (size_t)Stage::shared_bytes(nb);
