@@ -37,20 +37,4 @@ class DeviceOnce {
     std::atomic<uint64_t> mask_{0};
 };
 
-// Compute units of the current device, cached per device (0 if HIP cannot
-// tell).  Two threads racing through the first call both query HIP.
-inline int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c) return c;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
 }  // namespace kq

@@ -390,32 +390,26 @@ struct Plan {
     int tstep;  // tokens between consecutive units of a lane
 };
 
-// Units per lane.  More units per lane amortise the per-block constant setup
-// (fewer VALU instructions per unit) but leave fewer waves.  For the
-// Kronecker stage one unit per lane wins as long as all the launch's waves
-// are resident at once (occupancy 7, about 65 VGPRs): 3-8 % faster than 2, 4
-// or 8 on 4608 x 3072 (6912 waves) and 8-25 % on 8192 x 1152.  When one unit
-// per lane would take several rounds of waves, two per lane win: about 4 %
-// on 4608 x 12288 (27648 waves at one per lane).  A stage can ask for its own
-// count (kUnitsPerLane): the scaling stage's 128 bytes of multipliers per
+// Units per lane: one unless the stage asks for more (kUnitsPerLane).  More
+// units per lane amortise the per-block constant setup (fewer VALU
+// instructions per unit) but leave fewer waves.  For the Kronecker stage one
+// unit per lane measured fastest: 3-8 % faster than 2, 4 or 8 on 4608 x 3072
+// (all 6912 waves resident at once), 8-25 % on 8192 x 1152, and still 3 %
+// faster than two per lane on 4608 x 12288, where one per lane takes about
+// four rounds of waves.  The scaling stage's 128 bytes of multipliers per
 // block make four per lane the better choice at every size (8.8 against
 // 9.0 us on 4608 x 3072, 29.7 against 36.5 us on 4608 x 12288).
-// KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides all of it for sweeps.
+// KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
 template <class S, class = void>
-struct stage_units : std::integral_constant<int, 0> {};
+struct stage_units : std::integral_constant<int, 1> {};
 template <class S>
 struct stage_units<S, std::void_t<decltype(S::kUnitsPerLane)>>
     : std::integral_constant<int, S::kUnitsPerLane> {};
 
-constexpr int kResidentWavesPerSimd = 7;
-
-static int units_per_lane(int stage_default, int64_t units) {
+static int units_per_lane(int stage_default) {
     static const int v = env_override("KQ_UNITS_PER_LANE", 0,
                                       [](int p) { return p == 1 || p == 2 || p == 4 || p == 8; });
-    if (v) return v;
-    if (stage_default) return stage_default;
-    const int64_t resident = (int64_t)device_cus() * 4 * kResidentWavesPerSimd * 64;
-    return resident > 0 && units > resident ? 2 : 1;
+    return v ? v : stage_default;
 }
 
 static bool plan_launch(int64_t tokens, int nb, int nu, Plan &pl) {
@@ -456,8 +450,7 @@ template <class Src, class Stage, class Sink>
 static kq_status run(const Src &src, const float *stage, const Sink &sink, int64_t tokens, int nb,
                      void *stream) {
     Plan pl;
-    if (!plan_launch(tokens, nb, units_per_lane(stage_units<Stage>::value, tokens * nb), pl))
-        return KQ_ERR_SHAPE;
+    if (!plan_launch(tokens, nb, units_per_lane(stage_units<Stage>::value), pl)) return KQ_ERR_SHAPE;
     const int t = (int)tokens;
     size_t sh = 0;
     if constexpr (stage_shares<Stage>::value) sh = (size_t)Stage::shared_bytes(nb);
