@@ -397,8 +397,8 @@ struct Plan {
 // (all 6912 waves resident at once), 8-25 % on 8192 x 1152, and still 3 %
 // faster than two per lane on 4608 x 12288, where one per lane takes about
 // four rounds of waves.  The scaling stage's 128 bytes of multipliers per
-// block make four per lane the better choice at every size (8.8 against
-// 9.0 us on 4608 x 3072, 29.7 against 36.5 us on 4608 x 12288).
+// block make four per lane its better choice: 29.2 against 38.7 us on
+// 4608 x 12288, equal (8.8 us) on 4608 x 3072.
 // KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
 template <class S, class = void>
 struct stage_units : std::integral_constant<int, 1> {};
