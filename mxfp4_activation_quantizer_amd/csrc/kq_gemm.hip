@@ -466,11 +466,17 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t *l) {
 }
 // A 16-byte LDS DMA the compiler does not track.  M0 holds the LDS base
 // (lane l writes at M0 + 16 l); one wait state must separate the write of
-// M0 from the DMA that reads it.
+// M0 from the DMA that reads it.  The compiler reserves M0 and does not
+// preserve it around inline assembly (hence its warning, silenced here):
+// this is sound only while nothing else in the kernel uses M0, which a test
+// checks in the kernel's assembly.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_raw(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 struct PipePlan {
     int ga[kDA], gw[kDW];   // code offsets at K tile 0, as in DmaPlan
