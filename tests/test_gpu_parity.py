@@ -627,7 +627,10 @@ def _random_mxfp4(g, rows, k, lo=118, hi=128):
                                    # pipelined kernel (1536: an odd number of
                                    # scale pairs per tile; 4608 and 9216: two
                                    # and three passes of its 12-step loop)
-                                   (257, 513, 1536), (70, 260, 4608), (33, 520, 9216)])
+                                   (257, 513, 1536), (70, 260, 4608), (33, 520, 9216),
+                                   # a single output tile: seven of the eight
+                                   # XCD groups have no tile and leave at once
+                                   (1, 7, 1536), (3, 300, 3072)])
 def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     torch = torch_cuda
     g = np.random.default_rng(M * 7 + N * 3 + K)
