@@ -642,6 +642,30 @@ def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     _assert_gemm_close(yb, Y, B, K)
 
 
+def _sweep_shapes(n=24, seed=2024):
+    """Seeded GEMM shapes: M, N from 1 to 600, K any multiple of 128 up to
+    9216, a third of them multiples of 1536 (the pipelined kernel)."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        m, nn = int(g.integers(1, 601)), int(g.integers(1, 601))
+        k = int(g.integers(1, 7)) * 1536 if i % 3 == 0 else int(g.integers(1, 73)) * 128
+        out.append((m, nn, k))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _sweep_shapes())
+def test_gemm_shape_sweep(torch_cuda, M, N, K):
+    torch = torch_cuda
+    g = np.random.default_rng(M * 131 + N * 17 + K)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    Y, B = _gemm_reference(ac, as_, wc, ws)
+    _assert_gemm_close(yb, Y, B, K)
+
+
 @pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8),
                                        (70, 260, 768, 12), (70, 260, 1536, 12)])
 def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
