@@ -516,6 +516,33 @@ def test_dequant_inverse_ragged(torch_cuda, tokens, nb):
     _inverse_vs_definition(c, s, lu, got)
 
 
+def _quant_sweep_shapes(n=24, seed=77):
+    """Seeded (tokens, blocks, row padding): tokens 1..3000, blocks 1..400,
+    padding 0, 8 or 24 elements."""
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(1, 3001)), int(g.integers(1, 401)), int(g.choice([0, 8, 24])))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("tokens,nb,pad", _quant_sweep_shapes())
+def test_quantizer_and_inverse_shape_sweep(torch_cuda, tokens, nb, pad):
+    """Random shapes through the quantizer (bit-exact with the oracle's fixed
+    fp32 order, strided rows with NaN padding never read) and back through
+    the inverse (bit-exact as well)."""
+    g = np.random.default_rng(tokens * 13 + nb * 7 + pad)
+    d = nb * 32
+    xf = g.standard_normal((tokens, d + pad)) * np.exp(g.standard_normal((tokens, 1)))
+    x = inputs.f64_to_bf16_bits(xf)
+    x[:, d:] = 0x7FC0
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    c, s = kq.transform_quant(to_gpu_bf16(x), to_gpu(lu), d=d)
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32, d=d)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+    got = _gpu_dequant_inverse(wc, ws, lu)
+    np.testing.assert_array_equal(got, oracle.dequant_inverse(wc, ws, lu, oracle.STAGED32))
+
+
 @pytest.mark.parametrize("tokens,nb,pad", [(5, 3, 8), (70, 1, 24), (131, 7, 16)])
 def test_dequant_inverse_strided_output_leaves_padding(torch_cuda, tokens, nb, pad):
     """Row stride beyond d: every unit lands at its row's offset (the stores
