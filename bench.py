@@ -600,7 +600,8 @@ def main() -> int:
         wg = gemm["weight_bytes"] / (pms * 1e-3) / 1e9
         extra["weight_quant"] = {"ms_per_step": round(pms, 6), "shape": [gemm["n"], gemm["k"]],
                                  "GBps": round(wg, 1), "frac_of_hbm_peak": round(wg / PEAK_HBM_GBS, 4)}
-        pms = timed("kq_w4a4_gemm", max(10, args.steps // 10), max(2, args.warmup // 10))
+        # at least 50 launches (6 ms): the GEMM's clock moves with its power draw
+        pms = timed("kq_w4a4_gemm", max(50, args.steps // 4), max(5, args.warmup // 10))
         tf = gemm["flops"] / (pms * 1e-3) / 1e12
         if "theta" in gemm:
             # end-to-end error of W4A4 against the unquantised X W^T on 24
