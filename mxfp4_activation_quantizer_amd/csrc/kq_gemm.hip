@@ -51,10 +51,10 @@
 // and every wave stores two whole 512-byte tile rows per instruction.
 //
 // All of the above describes the per-tile kernel, which takes any K that is
-// a multiple of 128.  A K that is a multiple of 1536 takes the pipelined
-// kernel further down: the same tiles, MFMAs and epilogue, with the K
-// pipeline carried across output tiles and the scales in a ring of their
-// own.
+// a multiple of 128.  A K that is a multiple of 512, with 16-byte aligned
+// scale arrays, takes the pipelined kernel further down: the same tiles,
+// MFMAs and epilogue, with the K pipeline carried across output tiles and
+// the scales in a ring of their own.
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -421,12 +421,13 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined form for K a multiple of six K tiles (K % 1536 == 0): every
-// output tile starts at stage 0, K tile k of any tile sits in stage k % 3,
-// and the pipeline runs on across output tiles.  The last two steps of a
-// tile issue the next tile's first two K tiles, and the epilogue runs in
-// stage 2 (its last K tile's, free once multiplied) while those are in
-// flight: no pipeline fill per tile and no idle epilogue.
+// Pipelined form for K a multiple of two K tiles (K % 512 == 0) and 16-byte
+// aligned scale arrays: the K pipeline runs on across the output tiles of a
+// workgroup.  K tile g of the workgroup's running sequence sits in stage
+// g % 3, so a tile's first K tile is in stage (its index * KT) % 3.  The last
+// two steps of a tile issue the next tile's first two K tiles, and the
+// epilogue runs in the stage of its last K tile (free once multiplied) while
+// those are in flight: no pipeline fill per tile and no idle epilogue.
 //
 // Scales travel apart from the codes.  One row's scale bytes for two
 // consecutive K tiles are 16 contiguous bytes, so with every even K tile one
@@ -451,14 +452,12 @@ constexpr int kPStage = kAB + kWB;                               // codes of one
 constexpr int kRingRows = kBM + kBN;                             // A rows, then W rows
 constexpr int kRingSlot = 16 * kRingRows;                        // 6144
 constexpr int kRingRowsPerWave = kRingRows / (kGemmThreads / 64);  // 48
-constexpr int kPipeK = 6 * kBK;                                  // K granule of this kernel
+constexpr int kPipeK = 2 * kBK;                                  // K granule of this kernel
 static_assert(kRingRows % (kGemmThreads / 64) == 0 && kRingRowsPerWave <= 64, "one scale DMA per wave");
 static_assert(3 * kPStage + 2 * kRingSlot <= 160 * 1024, "LDS of the pipelined kernel");
 static_assert(kDA + kDW == 6, "six code DMAs per step");
 
-__shared__ __attribute__((aligned(16))) uint8_t gp_st0[kPStage];
-__shared__ __attribute__((aligned(16))) uint8_t gp_st1[kPStage];
-__shared__ __attribute__((aligned(16))) uint8_t gp_st2[kPStage];
+__shared__ __attribute__((aligned(16))) uint8_t gp_st[3 * kPStage];
 __shared__ __attribute__((aligned(16))) uint8_t gp_ring[2 * kRingSlot];
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t *l) {
@@ -559,6 +558,9 @@ __device__ __forceinline__ void pipe_compute(const uint8_t *__restrict__ b, cons
     gemm_kstep<3>(b, wm, wn, i32, kg, sa, sw, acc);
 }
 
+// kFixedStages: KT is a multiple of 3, so every tile's K tile 0 is in
+// stage 0 and the stage of each unrolled step is a constant.
+template <bool kFixedStages>
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, uint16_t *__restrict__ y,
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     const int wm = wave / kGemmWN, wn = wave % kGemmWN;
     const int i32 = lane & 31, kg = lane >> 5;
     const int K2 = K / 2, K32 = K / 32;
-    const int KT = K / kBK;              // a multiple of 6
+    const int KT = K / kBK;              // even
     const int flip = (KT / 2) & 1;       // ring slot change from one tile's pair 0 to the next's
 
     int m0, n0;
@@ -581,8 +583,10 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
     PipePlan pc;
     make_pipe_plan(pc, m0, n0, M, N, K2, K32, wave, lane, as, ws);
     int pb = 0;                          // ring slot of this tile's scale pair 0
-    pipe_issue(pc, ac, wc, 0, wave, lane, gp_st0, pb);
-    pipe_issue(pc, ac, wc, 1, wave, lane, gp_st1, pb);
+    int sb = 0;                          // stage of this tile's K tile 0
+    const int sstep = kFixedStages ? 0 : KT % 3;  // stage change from one tile's K tile 0 to the next's
+    pipe_issue(pc, ac, wc, 0, wave, lane, gp_st, pb);
+    pipe_issue(pc, ac, wc, 1, wave, lane, gp_st + kPStage, pb);
 
     f32x16g acc[2][2];
     u32x4 sc[4];  // scale words of the current pair, rows A j = 0, 1 and W i = 0, 1
@@ -603,18 +607,22 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x16g{};
 
-        // step s: retire K tile s, multiply K tile s from stage s % 3 and,
-        // halfway through, issue K tile s + 2 (or the next tile's s + 2 - KT)
-        // into stage (s + 2) % 3.  Twelve steps per pass keep both the stage
-        // (s % 3) and the parity of s fixed for each unrolled step.
+        // step s: retire K tile s, multiply K tile s from stage (sb + s) % 3
+        // and, halfway through, issue K tile s + 2 (or the next tile's
+        // s + 2 - KT) into stage (sb + s + 2) % 3.  Twelve steps per pass
+        // keep the parity of s and the stage offset (s % 3) of each unrolled
+        // step fixed; the pass's three stage addresses are taken once.
         constexpr int kSteps = 12;
         for (int s0 = 0; s0 < KT; s0 += kSteps) {
+            const int r0 = kFixedStages ? 0 : (sb + s0) % 3;
+            const uint8_t *sp[3] = {gp_st + r0 * kPStage, gp_st + (r0 == 2 ? 0 : r0 + 1) * kPStage,
+                                    gp_st + (r0 == 0 ? 2 : r0 - 1) * kPStage};
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
                 const int st = s0 + u;
                 if (st >= KT) break;
-                const uint8_t *in = u % 3 == 1 ? gp_st0 : u % 3 == 2 ? gp_st1 : gp_st2;
-                const uint8_t *rd = u % 3 == 0 ? gp_st0 : u % 3 == 1 ? gp_st1 : gp_st2;
+                const uint8_t *in = sp[(u + 2) % 3];
+                const uint8_t *rd = sp[u % 3];
                 // the step before issued 6 DMAs, 7 when its K tile (s + 1) was even
                 if (u & 1) KQ_WAIT_VM(kDA + kDW + 1);
                 else KQ_WAIT_VM(kDA + kDW);
@@ -630,14 +638,16 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_pipe_kernel(
                              });
             }
         }
-        // epilogue in stage 2 (K tile KT - 1's, KT a multiple of 3), two
-        // passes of 64 rows (j = 0: rows 0-31 and 64-95, j = 1: the others);
-        // stages 0 and 1 take the next tile's first K tiles
+        // epilogue in the stage of K tile KT - 1, two passes of 64 rows
+        // (j = 0: rows 0-31 and 64-95, j = 1: the others); the other two
+        // stages take the next tile's first K tiles
+        uint8_t *ep = gp_st + (kFixedStages ? 2 : (sb + KT - 1) % 3) * kPStage;
         __builtin_amdgcn_s_barrier();
-        store_half(acc, 0, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_half(acc, 0, ep, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         __builtin_amdgcn_s_barrier();
-        store_half(acc, 1, gp_st2, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
+        store_half(acc, 1, ep, wm, wn, i32, kg, tid, m0, n0, M, N, ldy, y, barrier);
         if (!has_next) break;
+        sb = (sb + sstep) % 3;
         t = tn;
         m0 = m1;
         n0 = n1;
@@ -674,18 +684,27 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
     static const int pipe_env = env_override("KQ_GEMM_PIPE", 1, [](int v) { return v == 0 || v == 1; });
-    const bool pipe = pipe_env && K % kPipeK == 0;
-    const void *fn = pipe ? (const void *)w4a4_gemm_pipe_kernel : (const void *)w4a4_gemm_kernel;
+    // the pipelined kernel fetches two K tiles' scale bytes per row with one
+    // 16-byte DMA: it needs 16-byte aligned scale rows (K % 512 == 0 and
+    // 16-byte aligned arrays); otherwise the per-tile kernel runs
+    const bool pipe = pipe_env && K % kPipeK == 0 && (uintptr_t)as % 16 == 0 &&
+                      (uintptr_t)ws % 16 == 0;
+    const void *fn = !pipe ? (const void *)w4a4_gemm_kernel
+                     : (K / kBK) % 3 == 0 ? (const void *)w4a4_gemm_pipe_kernel<true>
+                                         : (const void *)w4a4_gemm_pipe_kernel<false>;
     // The explicit vmcnt waits count this kernel's DMAs; register spills would
     // add scratch loads and stores to that count and let a stage be read
     // before it has landed.  A build that gives the kernel scratch memory is
     // refused rather than run.
     static const bool no_scratch = [] {
-        hipFuncAttributes fa, fb;
-        return hipFuncGetAttributes(&fa, (const void *)w4a4_gemm_kernel) == hipSuccess &&
-               fa.localSizeBytes == 0 &&
-               hipFuncGetAttributes(&fb, (const void *)w4a4_gemm_pipe_kernel) == hipSuccess &&
-               fb.localSizeBytes == 0;
+        const void *kernels[] = {(const void *)w4a4_gemm_kernel,
+                                 (const void *)w4a4_gemm_pipe_kernel<true>,
+                                 (const void *)w4a4_gemm_pipe_kernel<false>};
+        for (const void *k : kernels) {
+            hipFuncAttributes fa;
+            if (hipFuncGetAttributes(&fa, k) != hipSuccess || fa.localSizeBytes != 0) return false;
+        }
+        return true;
     }();
     if (!no_scratch) return KQ_ERR_HIP;
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,

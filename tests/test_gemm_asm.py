@@ -33,16 +33,19 @@ def test_pipelined_gemm_m0_only_in_dma_sequences(tmp_path):
            "--cuda-device-only", "-S", os.path.join(CSRC, "kq_gemm.hip"), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=300)
     asm = out.read_text()
-    name = re.search(r"^(_ZN2kq21w4a4_gemm_pipe_kernel\w*):", asm, re.M).group(1)
-    body = [l for l in _kernel_body(asm, name) if l and not l.startswith((".", "//"))]
-    dmas = 0
-    for i, line in enumerate(body):
-        if not re.search(r"\bm0\b", line):
-            continue
-        assert line.startswith("s_mov_b32 m0,"), f"M0 used outside a DMA sequence: {line!r}"
-        assert body[i + 1] == "s_nop 0", f"no wait state after the M0 write: {body[i + 1]!r}"
-        assert body[i + 2].startswith("global_load_lds_dwordx4"), f"M0 write not followed by a DMA: {body[i + 2]!r}"
-        dmas += 1
-    # and every DMA of the kernel comes from such a sequence
-    assert dmas > 0
-    assert dmas == sum(1 for l in body if l.startswith("global_load_lds"))
+    names = re.findall(r"^(_ZN2kq21w4a4_gemm_pipe_kernel\w*):", asm, re.M)
+    assert len(names) == 2, names  # fixed and moving stage mapping
+    for name in names:
+        body = [l for l in _kernel_body(asm, name) if l and not l.startswith((".", "//"))]
+        dmas = 0
+        for i, line in enumerate(body):
+            if not re.search(r"\bm0\b", line):
+                continue
+            assert line.startswith("s_mov_b32 m0,"), f"{name}: M0 used outside a DMA sequence: {line!r}"
+            assert body[i + 1] == "s_nop 0", f"{name}: no wait state after the M0 write: {body[i + 1]!r}"
+            assert body[i + 2].startswith("global_load_lds_dwordx4"), \
+                f"{name}: M0 write not followed by a DMA: {body[i + 2]!r}"
+            dmas += 1
+        # and every DMA of the kernel comes from such a sequence
+        assert dmas > 0
+        assert dmas == sum(1 for l in body if l.startswith("global_load_lds"))

@@ -647,14 +647,19 @@ def _random_mxfp4(g, rows, k, lo=118, hi=128):
                                    # K past one 15-step pass of the K pipeline
                                    # (3328), whole and ending in a half tile
                                    (70, 260, 4096), (33, 40, 4224), (5, 8, 7808),
-                                   # K a multiple of 768 but not of 1536:
-                                   # the per-tile kernel
+                                   # K not a multiple of 512: the per-tile
+                                   # kernel
                                    (130, 300, 768), (5, 17, 2304), (64, 256, 6912),
-                                   # K a multiple of 1536: the cross-tile
-                                   # pipelined kernel (1536: an odd number of
-                                   # scale pairs per tile; 4608 and 9216: two
-                                   # and three passes of its 12-step loop)
+                                   # K a multiple of 512: the cross-tile
+                                   # pipelined kernel (1536, 2560: an odd
+                                   # number of scale pairs per tile; 1024,
+                                   # 2048, 2560, 5120: a tile's first K tile
+                                   # moves from stage to stage; 4608 and
+                                   # 9216: two and three passes of its
+                                   # 12-step loop)
                                    (257, 513, 1536), (70, 260, 4608), (33, 520, 9216),
+                                   (100, 300, 1024), (129, 257, 2048), (40, 600, 2560),
+                                   (33, 520, 5120),
                                    # a single output tile: seven of the eight
                                    # XCD groups have no tile and leave at once
                                    (1, 7, 1536), (3, 300, 3072)])
@@ -711,14 +716,42 @@ def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     assert (inputs.bf16_bits_to_f32(yb[:, N:]) == 5.0).all()
 
 
-@pytest.mark.parametrize("K", [768, 1536, 3072])
+@pytest.mark.parametrize("K", [1024, 3072])
+def test_gemm_scales_only_4_byte_aligned(torch_cuda, K):
+    """Scale arrays 4-byte but not 16-byte aligned (the ABI's minimum): the
+    pipelined kernel's 16-byte scale DMAs cannot serve them, so the per-tile
+    kernel must run, and the result must be the same."""
+    torch = torch_cuda
+    M, N = 150, 300
+    g = np.random.default_rng(K + 5)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+
+    def off4(a):
+        buf = torch.zeros(a.size + 16, dtype=torch.uint8, device="cuda")
+        v = buf[4:4 + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(a).cuda())
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    y = kq.w4a4_gemm(to_gpu(ac), off4(as_), to_gpu(wc), off4(ws))
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    Y, B = _gemm_reference(ac, as_, wc, ws)
+    _assert_gemm_close(yb, Y, B, K)
+    y16 = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
+    np.testing.assert_array_equal(_np(y16.view(torch.int16)), _np(y.view(torch.int16)))
+
+
+@pytest.mark.parametrize("K", [768, 1536, 2048, 2560, 3072])
 def test_gemm_workgroups_walk_several_tiles(torch_cuda, K):
     """More output tiles (20 x 16 = 320) than workgroups (one per CU): the
     persistent workgroups walk several tiles.  K = 768 takes the per-tile
-    kernel; 1536 and 3072 the pipelined one, which carries the K pipeline and
-    the scale ring from one tile into the next (1536: three scale pairs per
-    tile, so the ring slot of a tile's first pair alternates; 3072: six).
-    Three rows of every M tile are checked over all N columns."""
+    kernel; the others the pipelined one, which carries the K pipeline and
+    the scale ring from one tile into the next: with 1536 and 2560 (three and
+    five scale pairs per tile) the ring slot of a tile's first pair
+    alternates, with 2048 and 2560 (8 and 10 K tiles) the stage of a tile's
+    first K tile moves on by 2 and 1.  Three rows of every M tile are checked
+    over all N columns."""
     torch = torch_cuda
     M, N = 2560, 4096
     g = np.random.default_rng(77 + K)
