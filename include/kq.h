@@ -197,6 +197,9 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
  *
  * K % 128 == 0; M and N are arbitrary, with max(M, N) * K/2 < 2^31 (one
  * operand's codes under 2 GiB).  M == 0 or N == 0 returns KQ_OK.
+ * With K % 512 == 0 and both scale arrays 16-byte aligned a faster kernel
+ * runs (the K pipeline continues across output tiles); the results are the
+ * same either way.
  * KQ_ERR_HIP also if the library was built so that the kernel needs scratch
  * memory (its load waits count its own loads and would be wrong then).
  */
