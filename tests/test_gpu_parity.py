@@ -742,15 +742,15 @@ def test_gemm_scales_only_4_byte_aligned(torch_cuda, K):
     np.testing.assert_array_equal(_np(y16.view(torch.int16)), _np(y.view(torch.int16)))
 
 
-@pytest.mark.parametrize("K", [768, 1536, 2048, 2560, 3072])
+@pytest.mark.parametrize("K", [512, 768, 1024, 1536, 2048, 2560, 3072])
 def test_gemm_workgroups_walk_several_tiles(torch_cuda, K):
     """More output tiles (20 x 16 = 320) than workgroups (one per CU): the
     persistent workgroups walk several tiles.  K = 768 takes the per-tile
     kernel; the others the pipelined one, which carries the K pipeline and
-    the scale ring from one tile into the next: with 1536 and 2560 (three and
-    five scale pairs per tile) the ring slot of a tile's first pair
-    alternates, with 2048 and 2560 (8 and 10 K tiles) the stage of a tile's
-    first K tile moves on by 2 and 1.  Three rows of every M tile are checked
+    the scale ring from one tile into the next: with 512, 1536 and 2560 (one,
+    three and five scale pairs per tile) the ring slot of a tile's first pair
+    alternates, with 512, 1024, 2048 and 2560 (2, 4, 8 and 10 K tiles) the
+    stage of a tile's first K tile moves on by 2, 1, 2 and 1.  Three rows of every M tile are checked
     over all N columns."""
     torch = torch_cuda
     M, N = 2560, 4096
