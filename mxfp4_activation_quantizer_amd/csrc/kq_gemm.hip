@@ -40,8 +40,8 @@
 // steps (one pass for K up to 3328).
 //
 // Workgroup order: XCD x (workgroups go to the 8 XCDs round-robin) takes a
-// contiguous range of an order that walks four M tiles for each N tile, so
-// each W tile is fetched into that XCD's L2 once for four workgroups.
+// contiguous range of an order that walks eight M tiles for each N tile, so
+// each W tile is fetched into that XCD's L2 once for eight workgroups.
 // A K that is a multiple of 128 but not of 256 ends with a half tile: its
 // missing half re-reads the valid half (never used) and only its first two
 // MFMA steps run.
@@ -76,7 +76,7 @@ constexpr int kBM = 64 * kGemmWM, kBN = 64 * kGemmWN;
 constexpr int kGemmThreads = 64 * kGemmWM * kGemmWN;
 constexpr int kBK = 256;                          // K elements per LDS tile
 constexpr int kRowBytes = kBK / 2;                // 128 code bytes per row per tile
-constexpr int kMGroup = 4;                        // M tiles that share a W tile
+constexpr int kMGroup = 8;                        // M tiles that share a W tile
 constexpr int kAB = kBM * kRowBytes, kWB = kBN * kRowBytes;
 
 __device__ __forceinline__ int swz_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
@@ -189,7 +189,7 @@ __device__ __forceinline__ void gemm_compute(const uint8_t *__restrict__ b, int 
     }
 }
 
-// Workgroup tile lin of the order that walks four M tiles for each N tile.
+// Workgroup tile lin of the order that walks kMGroup M tiles for each N tile.
 __device__ __forceinline__ void tile_origin(int lin, int mtc, int ntc, int &m0, int &n0) {
     const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
     const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     int M, int N, int K, int64_t ldy, int mtc, int ntc) {
     // ---- persistent: workgroup w of XCD x (workgroups go to the XCDs
     //      round-robin) takes tiles w, w + wpx, ... of that XCD's contiguous
-    //      range of an order that walks four M tiles for each N tile; its
+    //      range of an order that walks kMGroup M tiles for each N tile; its
     //      output stores drain while the next tile's first DMAs are in flight
     const int tiles = mtc * ntc, per = (tiles + 7) / 8, wpx = gridDim.x >> 3;
     for (int t = blockIdx.x >> 3; t < per; t += wpx) {
