@@ -3,6 +3,9 @@ from __future__ import annotations
 
 import numpy as np
 
+import oracle
+from mxfp4_activation_quantizer_amd import inputs
+
 # Midpoints of the E2M1 magnitude grid 0, .5, 1, 1.5, 2, 3, 4, 6.
 E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 E2M1_MAG = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
@@ -71,3 +74,26 @@ def assert_codes_within_tie_tolerance(codes_gpu, scales_gpu, codes_ref, scales_r
         assert np.all(near), "a code differs away from a rounding tie"
     assert n <= max_frac * cg.size, f"{n} codes differ (> {max_frac} of {cg.size})"
     return int(smis.sum()), n
+
+
+def gemm_reference(ac, as_, wc, ws):
+    A = oracle.mxfp4_dequant(ac, as_)
+    W = oracle.mxfp4_dequant(wc, ws)
+    Y = oracle.matmul_nt(A, W)
+    B = oracle.matmul_nt(np.abs(A), np.abs(W))
+    return Y, B
+
+
+def assert_gemm_close(y_bits, Y, B, K):
+    """bf16 of an fp32-accumulated sum of exact products: within half a bf16
+    step of the fp64 sum plus K * 2^-23 of sum |a||w| (fp32 accumulation).
+    Half a bf16 step is up to 2^-8 of the value, so the same bound holds
+    normwise; in addition at least 90 % of the outputs must equal the bf16
+    rounding (nearest even) of the fp64 sum itself."""
+    y = inputs.bf16_bits_to_f32(y_bits).astype(np.float64)
+    err = np.abs(y - Y)
+    tol = 2.0 ** -8 * np.abs(Y) + K * 2.0 ** -23 * B + 1e-30
+    assert np.all(err <= tol), f"{int((err > tol).sum())} outputs off"
+    assert np.linalg.norm(y - Y) <= 2.0 ** -8 * np.linalg.norm(Y) + K * 2.0 ** -23 * np.linalg.norm(B)
+    exact = np.mean(np.asarray(y_bits, np.uint16) == inputs.f64_to_bf16_bits(Y))
+    assert exact >= 0.9, f"only {exact:.3f} of the outputs are the rounded fp64 sum"

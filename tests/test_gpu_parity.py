@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 from mxfp4_activation_quantizer_amd import inputs, kq
-from parity import (assert_codes_within_tie_tolerance, to_gpu, to_gpu_bf16, unpack_codes,
-                    REL_Y)
+from parity import (assert_codes_within_tie_tolerance, assert_gemm_close, gemm_reference, to_gpu,
+                    to_gpu_bf16, unpack_codes, REL_Y)
 
 pytestmark = pytest.mark.gpu
 
@@ -613,29 +613,6 @@ def test_weight_quant_bit_exact_and_vs_definition(torch_cuda, rows, nb):
 # --------------------------------------------------------------------------
 # the W4A4 consumer
 # --------------------------------------------------------------------------
-def _gemm_reference(ac, as_, wc, ws):
-    A = oracle.mxfp4_dequant(ac, as_)
-    W = oracle.mxfp4_dequant(wc, ws)
-    Y = oracle.matmul_nt(A, W)
-    B = oracle.matmul_nt(np.abs(A), np.abs(W))
-    return Y, B
-
-
-def _assert_gemm_close(y_bits, Y, B, K):
-    """bf16 of an fp32-accumulated sum of exact products: within half a bf16
-    step of the fp64 sum plus K * 2^-23 of sum |a||w| (fp32 accumulation).
-    Half a bf16 step is up to 2^-8 of the value, so the same bound holds
-    normwise; in addition at least 90 % of the outputs must equal the bf16
-    rounding (nearest even) of the fp64 sum itself."""
-    y = inputs.bf16_bits_to_f32(y_bits).astype(np.float64)
-    err = np.abs(y - Y)
-    tol = 2.0 ** -8 * np.abs(Y) + K * 2.0 ** -23 * B + 1e-30
-    assert np.all(err <= tol), f"{int((err > tol).sum())} outputs off"
-    assert np.linalg.norm(y - Y) <= 2.0 ** -8 * np.linalg.norm(Y) + K * 2.0 ** -23 * np.linalg.norm(B)
-    exact = np.mean(np.asarray(y_bits, np.uint16) == inputs.f64_to_bf16_bits(Y))
-    assert exact >= 0.9, f"only {exact:.3f} of the outputs are the rounded fp64 sum"
-
-
 def _random_mxfp4(g, rows, k, lo=118, hi=128):
     codes = g.integers(0, 256, (rows, k // 2), dtype=np.uint8)
     scales = g.integers(lo, hi, (rows, k // 32), dtype=np.uint8)
@@ -670,8 +647,8 @@ def test_gemm_random_mxfp4(torch_cuda, M, N, K):
     wc, ws = _random_mxfp4(g, N, K)
     y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
     yb = _np(y.view(torch.int16)).view(np.uint16)
-    Y, B = _gemm_reference(ac, as_, wc, ws)
-    _assert_gemm_close(yb, Y, B, K)
+    Y, B = gemm_reference(ac, as_, wc, ws)
+    assert_gemm_close(yb, Y, B, K)
 
 
 def _sweep_shapes(n=24, seed=2024):
@@ -694,8 +671,8 @@ def test_gemm_shape_sweep(torch_cuda, M, N, K):
     wc, ws = _random_mxfp4(g, N, K)
     y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
     yb = _np(y.view(torch.int16)).view(np.uint16)
-    Y, B = _gemm_reference(ac, as_, wc, ws)
-    _assert_gemm_close(yb, Y, B, K)
+    Y, B = gemm_reference(ac, as_, wc, ws)
+    assert_gemm_close(yb, Y, B, K)
 
 
 @pytest.mark.parametrize("M,N,K,pad", [(37, 300, 256, 20), (130, 17, 128, 15), (5, 513, 384, 8),
@@ -711,8 +688,8 @@ def test_gemm_strided_output_leaves_padding(torch_cuda, M, N, K, pad):
     buf = torch.full((M, ld), 5.0, dtype=torch.bfloat16, device="cuda")
     kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws), y=buf[:, :N])
     yb = _np(buf.view(torch.int16)).view(np.uint16)
-    Y, B = _gemm_reference(ac, as_, wc, ws)
-    _assert_gemm_close(yb[:, :N], Y, B, K)
+    Y, B = gemm_reference(ac, as_, wc, ws)
+    assert_gemm_close(yb[:, :N], Y, B, K)
     assert (inputs.bf16_bits_to_f32(yb[:, N:]) == 5.0).all()
 
 
@@ -736,8 +713,8 @@ def test_gemm_scales_only_4_byte_aligned(torch_cuda, K):
 
     y = kq.w4a4_gemm(to_gpu(ac), off4(as_), to_gpu(wc), off4(ws))
     yb = _np(y.view(torch.int16)).view(np.uint16)
-    Y, B = _gemm_reference(ac, as_, wc, ws)
-    _assert_gemm_close(yb, Y, B, K)
+    Y, B = gemm_reference(ac, as_, wc, ws)
+    assert_gemm_close(yb, Y, B, K)
     y16 = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
     np.testing.assert_array_equal(_np(y16.view(torch.int16)), _np(y.view(torch.int16)))
 
@@ -760,8 +737,8 @@ def test_gemm_workgroups_walk_several_tiles(torch_cuda, K):
     y = kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws))
     yb = _np(y.view(torch.int16)).view(np.uint16)
     rows = np.array([mt * 128 + r for mt in range(M // 128) for r in (0, 61, 127)])
-    Y, B = _gemm_reference(ac[rows], as_[rows], wc, ws)
-    _assert_gemm_close(yb[rows], Y, B, K)
+    Y, B = gemm_reference(ac[rows], as_[rows], wc, ws)
+    assert_gemm_close(yb[rows], Y, B, K)
 
 
 def test_gemm_full_size_sampled_rows(torch_cuda):
@@ -779,8 +756,8 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
     yb = _np(y.view(torch.int16)).view(np.uint16)
     rows = np.sort(np.random.default_rng(9).choice(x.shape[0], 24, replace=False))
     acn, asn, wcn, wsn = _np(ac), _np(as_), _np(wc), _np(ws)
-    Y, B = _gemm_reference(acn[rows], asn[rows], wcn, wsn)
-    _assert_gemm_close(yb[rows], Y, B, x.shape[1])
+    Y, B = gemm_reference(acn[rows], asn[rows], wcn, wsn)
+    assert_gemm_close(yb[rows], Y, B, x.shape[1])
     # end to end against the unquantised product X W^T on the sampled rows
     xf = inputs.bf16_bits_to_f32(x[rows]).astype(np.float64)
     wf = inputs.bf16_bits_to_f32(w).astype(np.float64)
