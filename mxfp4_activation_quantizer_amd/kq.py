@@ -223,7 +223,7 @@ def _rows_out(t, name: str, device, dtype_name: str, rows: int, cols: int):
         raise ValueError(f"{name} must be a GPU tensor on {device}")
     if t.dtype != _dtype(dtype_name) or t.dim() != 2:
         raise ValueError(f"{name} must be a 2-D {_dtype(dtype_name)} tensor")
-    if t.shape[0] < rows or t.shape[1] < cols or (rows > 1 and t.stride(1) != 1):
+    if t.shape[0] < rows or t.shape[1] < cols or (cols > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be [>={rows}][>={cols}] with contiguous rows")
     return t
 

@@ -58,6 +58,10 @@ def test_outputs_and_operands_are_checked(torch_cuda):
     with pytest.raises(ValueError, match="y"):
         kq.w4a4_gemm(codes, scales, codes, scales, y=torch.empty((8, 8), dtype=torch.float32,
                                                                   device="cuda"))
+    # one output row whose columns are strided is refused as well
+    wide = torch.empty((1, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="y"):
+        kq.w4a4_gemm(codes[:1], scales[:1], codes, scales, y=wide[:, ::2])
     # a correct call still runs
     y = kq.w4a4_gemm(codes, scales, codes, scales)
     assert y.shape == (8, 8)
