@@ -65,3 +65,35 @@ def test_outputs_and_operands_are_checked(torch_cuda):
     # a correct call still runs
     y = kq.w4a4_gemm(codes, scales, codes, scales)
     assert y.shape == (8, 8)
+
+
+def test_calls_follow_the_current_stream(torch_cuda):
+    """Each call is queued on torch's current stream.  Quantizer, inverse and
+    GEMM calls interleaved on two side streams (default priority), each
+    stream working on its own tensors, give the results of the same calls
+    made one after another on the default stream."""
+    torch = torch_cuda
+    acts = inputs.activation("flux_attn")
+    lu = to_gpu(inputs.lu_params("flux_attn"))
+    xs = [to_gpu_bf16(acts[i * 200:(i + 1) * 200]) for i in range(4)]
+    wc, ws = kq.transform_quant(xs[3], lu)
+
+    def chain(x):
+        c, s = kq.transform_quant(x, lu)
+        return c, s, kq.dequant_inverse(c, s, lu), kq.w4a4_gemm(c, s, wc, ws)
+
+    want = [chain(x) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    got = [None] * len(xs)
+    for i, x in enumerate(xs):
+        with torch.cuda.stream(streams[i % 2]):
+            got[i] = chain(x)
+    torch.cuda.synchronize()
+    for g, w in zip(got, want):
+        for a, b in zip(g, w):
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b)
