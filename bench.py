@@ -91,6 +91,7 @@ rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o copy_WR
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ -o SQ -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_mfma -o SQ_mfma -- python3 bench.py --kernel-only --kernel kq_transform_quant_mfma --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_gemm -o SQ_gemm -- python3 bench.py --kernel-only --kernel kq_w4a4_gemm --steps 20 --warmup 5
+rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_adaln -o SQ_adaln -- python3 bench.py --kernel-only --kernel kq_adaln_transform_quant --steps 20 --warmup 5
 python3 bench.py --summarize-profiles OUT"""
 
 
@@ -183,9 +184,12 @@ def profile_commands(workload: str = "flux_attn") -> list:
     is not the default one (the copy calibration is the same for all)."""
     from mxfp4_activation_quantizer_amd import inputs
     gemm = inputs.WORKLOADS[workload].d == inputs.GEMM_K  # the consumer takes K = 3072
+    adaln = inputs.WORKLOADS[workload].d <= 8192          # one sample's vectors fit LDS
     out = []
     for c in PROFILE_COMMANDS.splitlines():
         if not gemm and "kq_w4a4_gemm" in c:
+            continue
+        if not adaln and "kq_adaln_transform_quant" in c:
             continue
         if workload != "flux_attn" and "bench.py --" in c and "--copy-calibration" not in c:
             c = c.replace("bench.py --", f"bench.py --workload {workload} --", 1)
@@ -284,13 +288,16 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
     with open(os.path.join(PROFILES, f"hbm_traffic_kq_transform_quant_{workload}.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
 
-    # instruction counters of the hot path and of the matrix-core arm
+    # instruction counters of the hot path, the matrix-core arm, the GEMM and
+    # the AdaLN-fused quantizer
     ctr = [f"# SQ counters per dispatch (mean over the dispatches), {workload} "
            f"{w.tokens}x{w.d}, from rocprofv3 --pmc",
            f"# kernel sources {src_hash}; commands:"]
     ctr += ["#   " + c for c in profile_commands(workload)]
     for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma"),
-                       ("SQ_gemm", "kq_w4a4_gemm")):
+                       ("SQ_gemm", "kq_w4a4_gemm"), ("SQ_adaln", "kq_adaln_transform_quant")):
+        if not any(f"OUT/{sub} " in c for c in profile_commands(workload)):
+            continue  # no such pass for this workload
         if not os.path.isdir(os.path.join(out_dir, sub)):
             ctr.append(f"{entry}: no {sub} pass in {out_dir}")
             continue
