@@ -136,3 +136,42 @@ def test_staged_matches_definition_within_the_forward_error_bound():
     bound = oracle.adaln_bound(x, sh, sc, lu, rows_per_sample=48)
     nsc, ncode = assert_codes_within_tie_tolerance(cs, ss, cd, sd, yd, bound)
     assert nsc <= 2
+
+
+def _ln_rows(x_bits, eps):
+    """fp64 LayerNorm of bf16 rows: (x - mean) / sqrt(var + eps), population
+    variance; also mean |x| and 1/sqrt(var + eps) per row."""
+    x = inputs.bf16_bits_to_f32(x_bits).astype(np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+    return (x - mu) * rstd, np.abs(x).mean(axis=1, keepdims=True), rstd
+
+
+def test_adaln_bound_closed_form_at_the_hadamard_start():
+    # At the Hadamard start every |T_ik| is 2^-5/2 (up to the fp32 rounding of
+    # 1/sqrt2 in the factors), so with shift = scale = 0 (h = n, the
+    # normalised value) the forward-error scale of every output k of block j
+    # is (sum_i 2|n_i| + 32 mean|x| rstd) / sqrt(32) over the block's inputs
+    # i.  A non-zero scale s multiplies it by |1 + s|; a shift c replaces
+    # |n_i| + |h_i| by |n_i| + |n_i + c|.
+    g = np.random.default_rng(11)
+    tokens, d, eps = 6, 256, 1e-6
+    x = _bits(g.normal(size=(tokens, d)) * g.lognormal(0, 0.5, size=(tokens, 1)) + 0.3)
+    lu = inputs.hadamard_init(d // 32)
+    n, amean, rstd = _ln_rows(x, eps)
+    z = np.zeros(d, np.float32)
+
+    def closed(e):  # e [tokens][d] -> per-output bound, constant over each block
+        blk = e.reshape(tokens, d // 32, 32).sum(axis=2) / np.sqrt(32.0)
+        return np.repeat(blk, 32, axis=1)
+
+    got = oracle.adaln_bound(x, z, z, lu, eps=eps)
+    want = closed(2 * np.abs(n) + amean * rstd)
+    assert np.allclose(got, want, rtol=1e-6, atol=0)
+    s = np.float32(0.75)
+    got_s = oracle.adaln_bound(x, z, np.full(d, s, np.float32), lu, eps=eps)
+    assert np.allclose(got_s, (1 + float(s)) * want, rtol=1e-6, atol=0)
+    c = np.float32(-1.5)
+    got_c = oracle.adaln_bound(x, np.full(d, c, np.float32), z, lu, eps=eps)
+    assert np.allclose(got_c, closed(np.abs(n) + amean * rstd + np.abs(n + float(c))),
+                       rtol=1e-6, atol=0)
