@@ -235,19 +235,25 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
 // but hold two or four blocks of centered values in registers (occupancy 3
 // or 2 instead of 7); on 4608 x 3072 one row per thread in workgroups of
 // about 384 threads measured fastest (17.0 us against 20.0 and 25.5 us).
-// KQ_ADALN_ROWS_PER_THREAD (1, 2 or 4; read once) overrides it for sweeps.
-static int adaln_rows_per_thread() {
-    static const int v = env_override("KQ_ADALN_ROWS_PER_THREAD", 1,
-                                      [](int q) { return q == 1 || q == 2 || q == 4; });
-    return v;
-}
+// Building with -DKQ_ADALN_ROWS_PER_THREAD=2 or 4 overrides it for sweeps.
+#ifndef KQ_ADALN_ROWS_PER_THREAD
+#define KQ_ADALN_ROWS_PER_THREAD 1
+#endif
+static_assert(KQ_ADALN_ROWS_PER_THREAD == 1 || KQ_ADALN_ROWS_PER_THREAD == 2 ||
+                  KQ_ADALN_ROWS_PER_THREAD == 4,
+              "KQ_ADALN_ROWS_PER_THREAD must be 1, 2 or 4");
+static int adaln_rows_per_thread() { return KQ_ADALN_ROWS_PER_THREAD; }
 
 // Row groups per workgroup: among G with G * nb <= 512 threads, the one whose
 // G * nb threads fill whole waves best; ties go to the G whose workgroup is
-// closest to KQ_ADALN_THREADS threads (default 384, read once; for sweeps).
+// closest to KQ_ADALN_THREADS threads (384 unless a sweep build sets it with
+// -DKQ_ADALN_THREADS=64..512).
+#ifndef KQ_ADALN_THREADS
+#define KQ_ADALN_THREADS 384
+#endif
+static_assert(KQ_ADALN_THREADS >= 64 && KQ_ADALN_THREADS <= 512, "KQ_ADALN_THREADS out of range");
 static int adaln_groups(int nb) {
-    static const int target =
-        env_override("KQ_ADALN_THREADS", 384, [](int v) { return v >= 64 && v <= 512; });
+    const int target = KQ_ADALN_THREADS;
     int best = 1;
     double best_util = -1.0;
     int best_dist = 1 << 30;

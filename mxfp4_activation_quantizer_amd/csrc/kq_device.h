@@ -40,10 +40,23 @@ __device__ __forceinline__ float block_amax(const float (&y)[32]) {
     return m;
 }
 
-// Correctly rounded fp32 reciprocal.  For |u| in [2^-126, 2^126) (biased
-// exponent 1..252) one fused correction of the hardware estimate,
-// r + r*(1 - u*r), equals IEEE 1/u bit for bit (checked exhaustively over all
-// fp32 inputs on gfx950); any other u takes the IEEE division.
+// floor(n / d) for 0 <= n < 2^31 by one 32x32 -> 64-bit multiply and a
+// shift: with s = 31 + ceil(log2 d) and m = ceil(2^s / d) (< 2^32, made once
+// on the host by div_magic), n*m / 2^s exceeds n/d by less than 2^-ceil(log2 d)
+// <= 1/d, which never reaches the next integer.
+struct DivMagic {
+    uint32_t m, s;
+};
+__host__ __device__ inline DivMagic div_magic(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t p = uint64_t(1) << (31 + l);
+    return DivMagic{(uint32_t)((p + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ uint32_t udiv31(uint32_t n, DivMagic dm) {
+    return (uint32_t)(((uint64_t)n * dm.m) >> dm.s);
+}
+
 // LDS position (in 16-B chunks) of chunk i (0..7) of block j's 32-float
 // slice of a per-channel vector staged in LDS.  Lane j reads its block's
 // eight chunks with a 128-B stride between lanes; XOR-ing the chunk index
@@ -52,6 +65,11 @@ __device__ __forceinline__ float block_amax(const float (&y)[32]) {
 // conflict-free.
 __device__ __forceinline__ int vec_chunk(int j, int i) { return j * 8 + (i ^ ((j >> 1) & 7)); }
 
+// Correctly rounded fp32 reciprocal.  For |u| in [2^-126, 2^126) (biased
+// exponent 1..252) one fused correction of the hardware estimate,
+// r + r*(1 - u*r), equals IEEE 1/u bit for bit (checked exhaustively over
+// that range on gfx950 against the correctly rounded quotient); any other u
+// takes the IEEE division.
 __device__ __forceinline__ float rcp_rn(float u) {
     const uint32_t ex = (__float_as_uint(u) >> 23) & 0xffu;
     if (__builtin_expect(ex - 1u < 252u, 1)) {
@@ -59,6 +77,28 @@ __device__ __forceinline__ float rcp_rn(float u) {
         return __builtin_fmaf(__builtin_fmaf(-u, r, 1.0f), r, r);
     }
     return 1.0f / u;
+}
+
+// The five reciprocals of a block's factor expansion, each equal to IEEE
+// 1/u_b: the corrected hardware estimate when every |u_b| lies in
+// [2^-126, 2^126) (one range test for all five, NaN failing it through the
+// NaN-propagating minimum/maximum), else the IEEE division for all five.
+__device__ __forceinline__ void rcp5_rn(const float (&u)[5], float (&iu)[5]) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const float r = __builtin_amdgcn_rcpf(u[b]);
+        iu[b] = __builtin_fmaf(__builtin_fmaf(-u[b], r, 1.0f), r, r);
+    }
+    const float a0 = __builtin_fabsf(u[0]), a1 = __builtin_fabsf(u[1]), a2 = __builtin_fabsf(u[2]),
+                a3 = __builtin_fabsf(u[3]), a4 = __builtin_fabsf(u[4]);
+    const float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(
+        __builtin_elementwise_minimum(a0, a1), a2), __builtin_elementwise_minimum(a3, a4));
+    const float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(a0, a1), a2), __builtin_elementwise_maximum(a3, a4));
+    if (__builtin_expect(!(mn >= 0x1p-126f && mx < 0x1p126f), 0)) {
+#pragma unroll
+        for (int b = 0; b < 5; ++b) iu[b] = 1.0f / u[b];
+    }
 }
 
 // E8M0 scale byte of the MXFP4 block: e = floor(log2 amax) - 2 clamped to

@@ -67,6 +67,16 @@
 
 namespace kq {
 
+// Sweep builds only: -DKQ_GEMM_WPX=n fixes the workgroups per XCD (0: one per
+// CU); -DKQ_GEMM_PIPE=0 keeps every call on the per-tile kernel.
+#ifndef KQ_GEMM_WPX
+#define KQ_GEMM_WPX 0
+#endif
+#ifndef KQ_GEMM_PIPE
+#define KQ_GEMM_PIPE 1
+#endif
+static_assert(KQ_GEMM_WPX >= 0, "KQ_GEMM_WPX must be >= 0");
+
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16g __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2g __attribute__((ext_vector_type(2)));
@@ -289,10 +299,8 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
     for (int t = blockIdx.x >> 3; t < per; t += wpx) {
         const int lin = (blockIdx.x & 7) * per + t;
         if (lin >= tiles) break;
-        const int blk = lin / (kMGroup * ntc), rem = lin - blk * kMGroup * ntc;
-        const int grp = mtc - blk * kMGroup < kMGroup ? mtc - blk * kMGroup : kMGroup;
-        const int nt = rem / grp, mt = blk * kMGroup + rem - nt * grp;
-        const int m0 = mt * kBM, n0 = nt * kBN;
+        int m0, n0;
+        tile_origin(lin, mtc, ntc, m0, n0);
 
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,32 +312,7 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_kernel(
 
         // ---- DMA plan: source offsets of this lane, one region per DMA ----
         DmaPlan pl;
-#pragma unroll
-        for (int q = 0; q < kDA; ++q) {
-            const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the A tile
-            const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-            pl.ga[q] = (m0 + row < M ? m0 + row : M - 1) * K2 + 16 * c;
-            pl.hia[q] = c >= 4;
-        }
-#pragma unroll
-        for (int q = 0; q < kDW; ++q) {
-            const int p = (q * (kGemmThreads / 64) + wave) * 64 + lane;
-            const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-            pl.gw[q] = (n0 + row < N ? n0 + row : N - 1) * K2 + 16 * c;
-            pl.hiw[q] = c >= 4;
-        }
-#pragma unroll
-        for (int q = 0; q < kDS; ++q) {
-            int r = q * (kGemmThreads / 64) + wave;
-            r = r < kDSRegions ? r : r - (kGemmThreads / 64);  // past the last: a repeat
-            pl.rs[q] = r;
-            const int dw = r * 64 + lane, v = dw >> 1, hf = dw & 1;  // row slot, dword of its 8 bytes
-            const int ra = m0 + v < M ? m0 + v : M - 1;
-            const int rw = n0 + (v - kBM) < N ? n0 + (v - kBM) : N - 1;
-            pl.sb[q] = v < kBM ? as : ws;
-            pl.gs[q] = (v < kBM ? ra : rw) * K32 + 4 * hf;
-            pl.his[q] = hf;
-        }
+        make_plan(pl, m0, n0, M, N, K2, K32, wave, lane, as, ws);
 
         auto issue = [&](int kt, uint8_t *st) {
             gemm_issue(pl, ac, wc, kt, half_tail && kt == KT - 1, wave, st);
@@ -666,8 +649,8 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     const int64_t tiles = (int64_t)mtc * ntc;
     if (tiles > INT32_MAX) return KQ_ERR_SHAPE;
     // one workgroup per CU (the LDS holds one), a multiple of the 8 XCDs;
-    // KQ_GEMM_WPX (read once) overrides the workgroups per XCD
-    static const int wpx_env = env_override("KQ_GEMM_WPX", 0, [](int v) { return v > 0; });
+    // a sweep build may fix the workgroups per XCD with -DKQ_GEMM_WPX=n
+    const int wpx_env = KQ_GEMM_WPX;
     static std::atomic<int> wpx_dev[64];  // per device; 0 = not yet known
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
@@ -683,7 +666,7 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
     const int64_t grid = 8 * (per < wpx ? per : wpx);
     void *args[] = {(void *)&ac, (void *)&as, (void *)&wc, (void *)&ws, (void *)&y, (void *)&M,
                     (void *)&N, (void *)&K, (void *)&ldy, (void *)&mtc, (void *)&ntc};
-    static const int pipe_env = env_override("KQ_GEMM_PIPE", 1, [](int v) { return v == 0 || v == 1; });
+    const bool pipe_env = KQ_GEMM_PIPE != 0;
     // the pipelined kernel fetches two K tiles' scale bytes per row with one
     // 16-byte DMA: it needs 16-byte aligned scale rows (K % 512 == 0 and
     // 16-byte aligned arrays); otherwise the per-tile kernel runs

@@ -1,24 +1,13 @@
-// kq_host.h — host-side helpers shared by the launch code: tuning overrides
-// read once from the environment, and once-per-device setup state.  All of
-// it is safe to use from several host threads at once.
+// kq_host.h — host-side helpers shared by the launch code: once-per-device
+// setup state, safe to use from several host threads at once.
 #pragma once
 
 #include <atomic>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <hip/hip_runtime.h>
 
 namespace kq {
-
-// The integer in environment variable `name` if `ok` accepts it, else `def`.
-// Call it from a function-local static initialiser, which runs once.
-inline int env_override(const char *name, int def, bool (*ok)(int)) {
-    const char *e = getenv(name);
-    if (!e) return def;
-    const int v = atoi(e);
-    return ok(v) ? v : def;
-}
 
 // Per-device flag for a setup step that must run once on each device (a
 // kernel attribute, a cached device property).  Two threads racing through

@@ -35,8 +35,8 @@ struct KronStage {
             l[b] = p[3 * b + 0];
             u[b] = p[3 * b + 1];
             w[b] = u[b] * p[3 * b + 2];
-            iu[b] = rcp_rn(u[b]);  // = IEEE 1/u
         }
+        rcp5_rn(u, iu);  // = IEEE 1/u
         // d_k as the running product over b = 0..4, built bit by bit.
         dk[0] = u[0];
         dk[1] = iu[0];
@@ -92,8 +92,8 @@ struct KronInvConsts {
             l[b] = p[3 * b + 0];
             u[b] = p[3 * b + 1];
             w[b] = u[b] * p[3 * b + 2];
-            iu[b] = rcp_rn(u[b]);
         }
+        rcp5_rn(u, iu);
         ek[0] = iu[0];
         ek[1] = u[0];
 #pragma unroll

@@ -204,11 +204,16 @@ __global__ __launch_bounds__(kMfmaThreads) void kron_mfma_kernel(
 // its tiles.  One tile per wave (more waves, more setup) measured faster up
 // to about a million units: 9.1 against 9.6 us on 4608 x 3072; two tiles
 // faster beyond: 29.2 against 32.4 us on 4608 x 12288.
-// KQ_MFMA_TILES_PER_WAVE (1, 2, 4 or 8; read once) overrides it for sweeps.
+// Building with -DKQ_MFMA_TILES_PER_WAVE=1, 2, 4 or 8 overrides it for sweeps.
+#ifndef KQ_MFMA_TILES_PER_WAVE
+#define KQ_MFMA_TILES_PER_WAVE 0
+#endif
+static_assert(KQ_MFMA_TILES_PER_WAVE == 0 || KQ_MFMA_TILES_PER_WAVE == 1 ||
+                  KQ_MFMA_TILES_PER_WAVE == 2 || KQ_MFMA_TILES_PER_WAVE == 4 ||
+                  KQ_MFMA_TILES_PER_WAVE == 8,
+              "KQ_MFMA_TILES_PER_WAVE must be 1, 2, 4 or 8");
 static int mfma_tiles_per_wave(int64_t units) {
-    static const int v = env_override("KQ_MFMA_TILES_PER_WAVE", 0,
-                                      [](int q) { return q == 1 || q == 2 || q == 4 || q == 8; });
-    if (v) return v;
+    if (KQ_MFMA_TILES_PER_WAVE) return KQ_MFMA_TILES_PER_WAVE;
     return units <= (int64_t(1) << 20) ? 1 : 2;
 }
 

@@ -314,18 +314,19 @@ struct FoldSink {
 template <class Src, class Stage, class Sink, int NU>
 __global__ __launch_bounds__(kBlockThreads) void block_kernel(Src src, const float *stage_param,
                                                               Sink sink,
-                                                              int tokens, int nb, int tstep) {
+                                                              int tokens, int nb, DivMagic nbm,
+                                                              int tstep) {
     Stage stage = Stage::from(stage_param);
     if constexpr (stage_shares<Stage>::value) stage.share(blockIdx.x * kBlockThreads, nb);
     const int g = blockIdx.x * kBlockThreads + threadIdx.x;
-    const int j = g % nb;
-    int t0 = g / nb;
+    int t0 = (int)udiv31((uint32_t)g, nbm);
+    const int j = g - t0 * nb;
     bool valid = true;
     if constexpr (Sink::kWave) {
         // the wave stores together: only a wave wholly past the end leaves;
         // its other lanes past the end redo the last row's unit and store
         // nothing
-        if ((g & ~63) / nb >= tokens) return;
+        if ((int)udiv31((uint32_t)(g & ~63), nbm) >= tokens) return;
         if (t0 >= tokens) {
             valid = false;
             t0 = tokens - 1;
@@ -399,7 +400,14 @@ struct Plan {
 // four rounds of waves.  The scaling stage's 128 bytes of multipliers per
 // block make four per lane its better choice: 29.2 against 38.7 us on
 // 4608 x 12288, equal (8.8 us) on 4608 x 3072.
-// KQ_UNITS_PER_LANE (1, 2, 4 or 8; read once) overrides it for sweeps.
+// Building with -DKQ_UNITS_PER_LANE=1, 2, 4 or 8 overrides it for sweeps.
+#ifndef KQ_UNITS_PER_LANE
+#define KQ_UNITS_PER_LANE 0
+#endif
+static_assert(KQ_UNITS_PER_LANE == 0 || KQ_UNITS_PER_LANE == 1 || KQ_UNITS_PER_LANE == 2 ||
+                  KQ_UNITS_PER_LANE == 4 || KQ_UNITS_PER_LANE == 8,
+              "KQ_UNITS_PER_LANE must be 1, 2, 4 or 8");
+
 template <class S, class = void>
 struct stage_units : std::integral_constant<int, 1> {};
 template <class S>
@@ -407,9 +415,7 @@ struct stage_units<S, std::void_t<decltype(S::kUnitsPerLane)>>
     : std::integral_constant<int, S::kUnitsPerLane> {};
 
 static int units_per_lane(int stage_default) {
-    static const int v = env_override("KQ_UNITS_PER_LANE", 0,
-                                      [](int p) { return p == 1 || p == 2 || p == 4 || p == 8; });
-    return v ? v : stage_default;
+    return KQ_UNITS_PER_LANE ? KQ_UNITS_PER_LANE : stage_default;
 }
 
 static bool plan_launch(int64_t tokens, int nb, int nu, Plan &pl) {
@@ -452,13 +458,14 @@ static kq_status run(const Src &src, const float *stage, const Sink &sink, int64
     Plan pl;
     if (!plan_launch(tokens, nb, units_per_lane(stage_units<Stage>::value), pl)) return KQ_ERR_SHAPE;
     const int t = (int)tokens;
+    const DivMagic nbm = div_magic((uint32_t)nb);
     size_t sh = 0;
     if constexpr (stage_shares<Stage>::value) sh = (size_t)Stage::shared_bytes(nb);
     switch (pl.nu) {
-        case 1: return launch(block_kernel<Src, Stage, Sink, 1>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
-        case 2: return launch(block_kernel<Src, Stage, Sink, 2>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
-        case 8: return launch(block_kernel<Src, Stage, Sink, 8>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
-        default: return launch(block_kernel<Src, Stage, Sink, 4>, pl, sh, stream, src, stage, sink, t, nb, pl.tstep);
+        case 1: return launch(block_kernel<Src, Stage, Sink, 1>, pl, sh, stream, src, stage, sink, t, nb, nbm, pl.tstep);
+        case 2: return launch(block_kernel<Src, Stage, Sink, 2>, pl, sh, stream, src, stage, sink, t, nb, nbm, pl.tstep);
+        case 8: return launch(block_kernel<Src, Stage, Sink, 8>, pl, sh, stream, src, stage, sink, t, nb, nbm, pl.tstep);
+        default: return launch(block_kernel<Src, Stage, Sink, 4>, pl, sh, stream, src, stage, sink, t, nb, nbm, pl.tstep);
     }
 }
 
