@@ -108,6 +108,20 @@ kq_status kq_transform_quant_mfma(const void *x, int64_t tokens, int64_t d, int6
                                   void *stream);
 
 /*
+ * kq_transform_quant_quad — the same quantizer with another work split:
+ * four lanes per unit (token, block), each holding 8 consecutive elements,
+ * the in-block index bits 3 and 4 exchanged between the lanes of a quad by
+ * DPP permutations (every wave load reads 1 KB of contiguous input).  Same
+ * transform (KroQuant summary, "Approach"), same fixed fp32 order and the
+ * same outputs, bit for bit, as kq_transform_quant; kept as the measured
+ * alternative layout.  Same arguments, layouts and errors as
+ * kq_transform_quant, and KQ_ERR_SHAPE when tokens * d/32 >= 2^31 - 256.
+ */
+kq_status kq_transform_quant_quad(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
+                                  const float *lu, uint8_t *codes, uint8_t *scales,
+                                  void *stream);
+
+/*
  * kq_transform_f32 — the same device transform as kq_transform_quant with an
  * fp32 store instead of the quantizer: y fp32 [tokens][d], 16-byte aligned.
  * For checking the transform stage on its own.
@@ -325,6 +339,23 @@ kq_status kq_calib_es_run(const void *x, int64_t tokens, int64_t d, int64_t ld_x
  */
 kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x,
                           uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * kq_stream_ceiling — not a quantizer: an HBM reference with the
+ * quantizer's byte counts and a wave-contiguous access pattern of its own
+ * (each wave reads 4 KB as four 1 KB loads and writes 1 KB + 64 B), for
+ * measuring what the memory system sustains independently of the
+ * quantizer's one-lane-per-unit mapping.
+ *   src     16-byte aligned, units * 64 bytes, read
+ *   codes   units * 16 bytes (16-byte aligned), written with a fold of the
+ *           input; NULL for a read-only pass
+ *   scales  units bytes, written; for a read-only pass at least 1 byte, of
+ *           which byte 0 may be written
+ * 0 <= units <= 2^36; units == 0 returns KQ_OK.  Output bytes are no
+ * quantization.
+ */
+kq_status kq_stream_ceiling(const void *src, int64_t units, uint8_t *codes, uint8_t *scales,
+                            void *stream);
 
 #ifdef __cplusplus
 }

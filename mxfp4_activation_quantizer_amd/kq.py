@@ -33,6 +33,7 @@ SIGNATURES = {
     "kq_version": (ctypes.c_int, []),
     "kq_transform_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_transform_quant_mfma": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kq_transform_quant_quad": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_transform_f32": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "kq_smooth_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kq_fwht32_quant": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
@@ -49,6 +50,7 @@ SIGNATURES = {
     "kq_calib_es_step": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kq_calib_es_run": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _P]),
     "kq_copy_ceiling": (_ST, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "kq_stream_ceiling": (_ST, [_P, _I64, _P, _P, _P]),
 }
 
 
@@ -100,6 +102,10 @@ def kq_transform_quant(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> in
 
 def kq_transform_quant_mfma(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> int:
     return lib().kq_transform_quant_mfma(x, tokens, d, ld_x, lu, codes, scales, stream)
+
+
+def kq_transform_quant_quad(x, tokens, d, ld_x, lu, codes, scales, stream=None) -> int:
+    return lib().kq_transform_quant_quad(x, tokens, d, ld_x, lu, codes, scales, stream)
 
 
 def kq_transform_f32(x, tokens, d, ld_x, lu, y, stream=None) -> int:
@@ -164,6 +170,10 @@ def kq_calib_es_run(x, tokens, d, ld_x, gram, theta, sigma, fbest, cand, noise, 
 
 def kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream=None) -> int:
     return lib().kq_copy_ceiling(x, tokens, d, ld_x, codes, scales, stream)
+
+
+def kq_stream_ceiling(src, units, codes, scales, stream=None) -> int:
+    return lib().kq_stream_ceiling(src, units, codes, scales, stream)
 
 
 # ---- tensor helpers --------------------------------------------------------
@@ -267,6 +277,18 @@ def transform_quant_mfma(x, lu, d: int | None = None, codes=None, scales=None):
     return codes, scales
 
 
+def transform_quant_quad(x, lu, d: int | None = None, codes=None, scales=None):
+    """The same quantizer with four lanes per unit (cross-lane upper stages)."""
+    tokens, ld = _act(x, "bf16")
+    d = x.shape[1] if d is None else d
+    codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
+    _lu(lu, x.device, d)
+    _check("kq_transform_quant_quad", kq_transform_quant_quad(
+        x.data_ptr(), tokens, d, ld, lu.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+        _stream(x)))
+    return codes, scales
+
+
 def transform_f32(x, lu, d: int | None = None, y=None):
     torch = _torch()
     tokens, ld = _act(x, "bf16")
@@ -315,6 +337,31 @@ def copy_ceiling(x, d: int | None = None, codes=None, scales=None):
     codes, scales = _mxfp4_out(x, tokens, d, codes, scales)
     _check("kq_copy_ceiling", kq_copy_ceiling(
         x.data_ptr(), tokens, d, ld, codes.data_ptr(), scales.data_ptr(), _stream(x)))
+    return codes, scales
+
+
+def stream_ceiling(src, codes=None, scales=None):
+    """HBM reference pass over ``src`` (a contiguous GPU tensor of
+    ``units * 64`` bytes): reads it and, when ``codes`` is given, writes
+    ``units * 16`` bytes there and ``units`` bytes into ``scales``."""
+    torch = _torch()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 64:
+        raise ValueError("src must hold a whole number of 64-byte units")
+    units = nbytes // 64
+    if scales is None:
+        scales = torch.empty(units if codes is not None else 1, dtype=torch.uint8,
+                             device=src.device)
+    if codes is not None:
+        _param(codes, "codes", src.device, "u8", units * 16)
+        _param(scales, "scales", src.device, "u8", units)
+    else:
+        _param(scales, "scales", src.device, "u8", 1)
+    _check("kq_stream_ceiling", kq_stream_ceiling(
+        src.data_ptr(), units, codes.data_ptr() if codes is not None else None,
+        scales.data_ptr(), _stream(src)))
     return codes, scales
 
 

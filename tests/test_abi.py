@@ -40,6 +40,8 @@ QUANT_CALLS = {
     "kq_transform_quant": lambda x, t, d, ld, c, s: kq.kq_transform_quant(x, t, d, ld, A16, c, s),
     "kq_transform_quant_mfma": lambda x, t, d, ld, c, s: kq.kq_transform_quant_mfma(
         x, t, d, ld, A16, c, s),
+    "kq_transform_quant_quad": lambda x, t, d, ld, c, s: kq.kq_transform_quant_quad(
+        x, t, d, ld, A16, c, s),
     "kq_smooth_quant": lambda x, t, d, ld, c, s: kq.kq_smooth_quant(x, t, d, ld, A16, c, s),
     "kq_weight_quant": lambda x, t, d, ld, c, s: kq.kq_weight_quant(x, t, d, ld, A16, c, s),
     "kq_fwht32_quant": lambda x, t, d, ld, c, s: kq.kq_fwht32_quant(x, t, d, ld, c, s),
@@ -78,6 +80,18 @@ def test_parameter_pointer_checks():
     assert kq.kq_transform_quant(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
     assert kq.kq_transform_quant_mfma(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
     assert kq.kq_transform_quant_mfma(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
+    assert kq.kq_transform_quant_quad(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
+    assert kq.kq_transform_quant_quad(A16, 4, 64, 64, ODD, A16, A16) == kq.KQ_ERR_ALIGN
+    # unit indices of the quad-lane kernel are 32-bit
+    assert kq.kq_transform_quant_quad(A16, 1 << 25, 2048, 2048, A16, A16, A16) == kq.KQ_ERR_SHAPE
+    sc = kq.kq_stream_ceiling
+    assert sc(None, 0, None, None) == kq.KQ_OK
+    assert sc(A16, -1, A16, A16) == kq.KQ_ERR_SHAPE
+    assert sc(A16, (1 << 36) + 1, A16, A16) == kq.KQ_ERR_SHAPE
+    assert sc(None, 4, A16, A16) == kq.KQ_ERR_NULL
+    assert sc(A16, 4, None, None) == kq.KQ_ERR_NULL       # read-only still needs scales
+    assert sc(ODD, 4, A16, A16) == kq.KQ_ERR_ALIGN
+    assert sc(A16, 4, A16 + 8, A16) == kq.KQ_ERR_ALIGN
     assert kq.kq_smooth_quant(A16, 4, 64, 64, None, A16, A16) == kq.KQ_ERR_NULL
     assert kq.kq_smooth_quant(A16, 4, 64, 64, A16 + 4, A16, A16) == kq.KQ_ERR_ALIGN
     assert kq.kq_transform_f32(A16, 4, 64, 64, A16, None) == kq.KQ_ERR_NULL

@@ -203,6 +203,49 @@ def test_shear_on_each_bit(torch_cuda):
         np.testing.assert_array_equal(y, oracle.transform(x, lu, oracle.STAGED32))
 
 
+def _rcp_sweep_u(seed=5, n_random=20000):
+    """u values for the reciprocal of the factor expansion: every biased
+    exponent 0..254 (0: zero and subnormals) with the significands all ones,
+    all zeros, top bit only, lowest bit only and four seeded random ones, both
+    signs; then seeded random finite bit patterns."""
+    g = np.random.default_rng(seed)
+    sig = [0x7FFFFF, 0, 0x400000, 1] + [int(v) for v in g.integers(0, 1 << 23, 4)]
+    bits = [(sgn << 31) | (e << 23) | m for e in range(255) for m in sig for sgn in (0, 1)]
+    rnd = (g.integers(0, 2, n_random).astype(np.uint64) << 31) | \
+        (g.integers(0, 255, n_random).astype(np.uint64) << 23) | \
+        g.integers(0, 1 << 23, n_random).astype(np.uint64)
+    return np.concatenate([np.array(bits, np.uint64), rnd]).astype(np.uint32).view(np.float32)
+
+
+def test_factor_reciprocal_every_exponent(torch_cuda):
+    """The kernel's 1/u (a corrected hardware reciprocal, IEEE division outside
+    the exponent range where the correction is exact) against the oracle's
+    IEEE division, bit for bit: block j has factor 0 = (0, u_j, 0) and the
+    identity elsewhere, and x = e_0 + e_1 in every block, so y_0 = u_j and
+    y_1 = 1/u_j.  Three rows of 24,080 blocks: 24,080 is not a multiple of 64,
+    so each u is handled at three different lanes of a wave."""
+    u = _rcp_sweep_u()
+    nb = u.size
+    lu = np.tile(IDENTITY, (nb, 5, 1)).astype(np.float32)
+    lu[:, 0, 1] = u
+    x = np.zeros((3, nb * 32), np.float64)
+    x[:, 0::32] = 1.0
+    x[:, 1::32] = 1.0
+    xb = inputs.f64_to_bf16_bits(x)
+    got = _np(kq.transform_f32(to_gpu_bf16(xb), to_gpu(lu)))
+    want = oracle.transform(xb, lu, oracle.STAGED32)
+    nan_g, nan_w = np.isnan(got), np.isnan(want)
+    np.testing.assert_array_equal(nan_g, nan_w)
+    np.testing.assert_array_equal(got.view(np.uint32)[~nan_g], want.view(np.uint32)[~nan_w])
+    # y_1 is exactly the IEEE reciprocal of every u, y_0 = u
+    with np.errstate(divide="ignore", over="ignore"):
+        recip = np.float32(1.0) / u
+    fin = ~np.isnan(recip)
+    for r in range(3):
+        np.testing.assert_array_equal(got[r, 1::32][fin].view(np.uint32), recip[fin].view(np.uint32))
+        np.testing.assert_array_equal(got[r, 0::32].view(np.uint32), u.view(np.uint32))
+
+
 # --------------------------------------------------------------------------
 # shapes, strides, edge cases
 # --------------------------------------------------------------------------
@@ -320,6 +363,105 @@ def test_copy_ceiling_touches_every_unit(torch_cuda):
     np.testing.assert_array_equal(_np(c).view(np.uint32).reshape(64, 8, 4), f)
     fs = np.bitwise_xor.reduce(f, axis=2) & 0xFF
     np.testing.assert_array_equal(_np(s), fs.astype(np.uint8))
+
+
+def test_stream_ceiling_reads_and_writes_every_unit(torch_cuda):
+    """The streaming reference: unit u's 16 output bytes are the XOR of the
+    16-byte chunks 64i + (u mod 64) (i = 0..3) of its wave's 4 KB, its byte
+    the low byte of their XOR; a read-only pass writes nothing but byte 0."""
+    torch = torch_cuda
+    g = np.random.default_rng(12)
+    units = 64 * 37 + 5                      # a ragged last wave
+    src = g.integers(0, 1 << 32, units * 16, dtype=np.uint64).astype(np.uint32)
+    sd = torch.from_numpy(src.view(np.int32)).to("cuda:0")
+    codes = torch.full((units * 16 + 32,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    scales = torch.full((units + 32,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    kq.stream_ceiling(sd, codes[:units * 16], scales[:units])
+    chunks = np.concatenate([src, np.zeros(64 * 16 * 4, np.uint32)]).reshape(-1, 4)  # 16-B chunks
+    want = np.empty((units, 4), np.uint32)
+    for u in range(units):
+        w0, lane = (u // 64) * 256, u % 64
+        want[u] = chunks[w0 + lane] ^ chunks[w0 + 64 + lane] ^ chunks[w0 + 128 + lane] ^ \
+            chunks[w0 + 192 + lane]
+    got = _np(codes)
+    np.testing.assert_array_equal(got[:units * 16].view(np.uint32).reshape(units, 4), want)
+    assert np.all(got[units * 16:] == 0xA5)
+    f = np.bitwise_xor.reduce(want, axis=1) & 0xFF
+    np.testing.assert_array_equal(_np(scales)[:units], f.astype(np.uint8))
+    assert np.all(_np(scales)[units:] == 0x5A)
+    one = torch.full((8,), 0x33, dtype=torch.uint8, device="cuda:0")
+    kq.stream_ceiling(sd, None, one)
+    o = _np(one)
+    assert np.all(o[1:] == 0x33) and o[0] in (0x33, 1)
+
+
+# --------------------------------------------------------------------------
+# the four-lanes-per-unit layout of the same quantizer
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("tokens,nb,pad", [(1, 1, 0), (3, 2, 8), (77, 3, 0), (129, 36, 0),
+                                           (65, 96, 8), (33, 97, 0), (5, 384, 16)])
+def test_quad_lane_quantizer_bit_exact(torch_cuda, tokens, nb, pad):
+    torch = torch_cuda
+    g = np.random.default_rng(tokens * 7 + nb)
+    d = nb * 32
+    x = inputs.f64_to_bf16_bits(g.standard_normal((tokens, d + pad)) *
+                                np.exp(g.standard_normal((tokens, 1))))
+    x[:, d:] = 0x7FC0
+    lu = (inputs.hadamard_init(nb) + g.normal(0, 0.2, (nb, 5, 3))).astype(np.float32)
+    cbuf = torch.full((tokens * d // 2 + 64,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    sbuf = torch.full((tokens * nb + 64,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    codes = cbuf[32:32 + tokens * d // 2].view(tokens, d // 2)
+    scales = sbuf[32:32 + tokens * nb].view(tokens, nb)
+    kq.transform_quant_quad(to_gpu_bf16(x), to_gpu(lu), d=d, codes=codes, scales=scales)
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32, d=d)
+    np.testing.assert_array_equal(_np(scales), ws)
+    np.testing.assert_array_equal(_np(codes), wc)
+    cb, sb = _np(cbuf), _np(sbuf)
+    assert np.all(cb[:32] == 0xA5) and np.all(cb[32 + tokens * d // 2:] == 0xA5)
+    assert np.all(sb[:32] == 0x5A) and np.all(sb[32 + tokens * nb:] == 0x5A)
+
+
+def test_quad_lane_quantizer_specials(torch_cuda):
+    nb = 4
+    x = np.full((8, nb * 32), 0x3F80, np.uint16)
+    x[0, 5] = 0x7FC0
+    x[1, 40] = 0x7F80
+    x[2, 70] = 0xFF80
+    x[3, 96:128] = 0x7F7F
+    x[4, :] = 0x0000
+    x[5, :] = 0x8000
+    x[6, 3::7] = 0x8000          # -0 mixed with ones
+    x[7, 8:24] = 0x0001          # bf16 subnormals
+    lu = inputs.hadamard_init(nb)
+    c, s = kq.transform_quant_quad(to_gpu_bf16(x), to_gpu(lu))
+    wc, ws = oracle.transform_quant(x, lu, oracle.STAGED32)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+    # identity parameters over every bf16 value
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(2048, 32)
+    lu1 = np.tile(IDENTITY, (1, 5, 1)).astype(np.float32)
+    c, s = kq.transform_quant_quad(to_gpu_bf16(allv), to_gpu(lu1))
+    wc, ws = oracle.transform_quant(allv, lu1, oracle.STAGED32)
+    np.testing.assert_array_equal(_np(s), ws)
+    np.testing.assert_array_equal(_np(c), wc)
+
+
+def test_quad_lane_quantizer_full_size_equals_one_lane(torch_cuda):
+    """At the FLUX attention-projection size the quad-lane kernel writes the
+    same bytes as kq_transform_quant everywhere, and sampled rows equal the
+    oracle's fixed order."""
+    x = inputs.activation("flux_attn")
+    lu = inputs.lu_params("flux_attn")
+    xd, ld = to_gpu_bf16(x), to_gpu(lu)
+    c1, s1 = kq.transform_quant(xd, ld)
+    c4, s4 = kq.transform_quant_quad(xd, ld)
+    c4, s4 = _np(c4), _np(s4)
+    np.testing.assert_array_equal(s4, _np(s1))
+    np.testing.assert_array_equal(c4, _np(c1))
+    rows = np.array([0, 1, 2047, 4607])
+    wc, ws = oracle.transform_quant(x[rows], lu, oracle.STAGED32)
+    np.testing.assert_array_equal(s4[rows], ws)
+    np.testing.assert_array_equal(c4[rows], wc)
 
 
 # --------------------------------------------------------------------------
