@@ -68,9 +68,11 @@ def load_traffic(kernel: str, workload: str, src_hash: str):
 KERNEL_MATCH = {
     "kq_transform_quant": "KronStage, kq::Mxfp4Sink",
     "kq_transform_quant_mfma": "kron_mfma_kernel",
+    "kq_transform_quant_quad": "kron_quad_kernel",
     "kq_smooth_quant": "SmoothStage, kq::Mxfp4Sink",
     "kq_fwht32_quant": "FwhtStage, kq::Mxfp4Sink",
     "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
+    "kq_stream_ceiling": "stream_kernel",
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
     "kq_w4a4_gemm": "w4a4_gemm_",  # the per-tile and the cross-tile pipelined kernel
@@ -324,6 +326,156 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
     return 0
 
 
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def round_trip_errors(kq, torch, inputs, np, held, xh, lu_d, start, theta, xa) -> dict:
+    """Relative Frobenius error ||x~ - x|| / ||x|| of the MXFP4 round trip on
+    the same held-out rows for every transform: the Kronecker transform with
+    the workload's random parameters, the Hadamard start and the calibrated
+    parameters (GPU quantizer, then the GPU dequantise + inverse, bf16 out),
+    per-channel scaling (codes / mult) and FWHT32 (codes times H_32, which is
+    its own inverse); the last two decode the GPU codes on the host and round
+    to bf16 like the Kronecker inverse."""
+    import scipy.linalg
+    out = {}
+    nx = float(np.linalg.norm(xh))
+    for name, lu in (("kron_random_params", lu_d), ("kron_hadamard_start", start),
+                     ("kron_calibrated", theta)):
+        c, s = kq.transform_quant(held, lu)
+        xr = kq.dequant_inverse(c, s, lu)
+        xr = inputs.bf16_bits_to_f32(xr.view(torch.int16).cpu().numpy().view(np.uint16))
+        out[name] = round(float(np.linalg.norm(xr.astype(np.float64) - xh)) / nx, 5)
+    tab = np.array(E2M1_VALUES + tuple(-v for v in E2M1_VALUES))
+
+    def decode(c, s):
+        c = c.cpu().numpy()
+        nib = np.empty((c.shape[0], c.shape[1] * 2), np.uint8)
+        nib[:, 0::2], nib[:, 1::2] = c & 15, c >> 4
+        e = np.repeat(s.cpu().numpy().astype(np.float64) - 127.0, 32, axis=1)
+        return tab[nib] * 2.0 ** e
+
+    mult = inputs.smooth_multipliers(xa)
+    c, s = kq.smooth_quant(held, torch.from_numpy(mult).to(held.device))
+    xs = decode(c, s) / mult.astype(np.float64)[None, :]
+    xs = inputs.bf16_bits_to_f32(inputs.f64_to_bf16_bits(xs)).astype(np.float64)
+    out["smooth"] = round(float(np.linalg.norm(xs - xh)) / nx, 5)
+    c, s = kq.fwht32_quant(held)
+    H = scipy.linalg.hadamard(32) / np.sqrt(32.0)
+    y = decode(c, s)
+    xf = (y.reshape(y.shape[0], -1, 32) @ H).reshape(y.shape)
+    xf = inputs.bf16_bits_to_f32(inputs.f64_to_bf16_bits(xf)).astype(np.float64)
+    out["fwht32"] = round(float(np.linalg.norm(xf - xh)) / nx, 5)
+    out["rows"] = "2048..2303 of the workload (held out from calibration)"
+    return out
+
+
+def graph_ms(torch, launch, n):
+    """ms per launch of n launches captured in one HIP graph (torch's
+    capture) and replayed: no host cost per launch."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            launch(i, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(n):
+            launch(i, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(3):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (3 * n)
+
+
+def hbm_ceilings(L, torch, dev, sp, xs, codes, scales, units, steps, warmup) -> dict:
+    """What the memory system sustains for the quantizer's traffic, measured
+    with kq_stream_ceiling (wave-contiguous loads and stores, no arithmetic, a
+    lane mapping of its own): at the workload's size over the same rotating
+    buffer sets (read only, and 64 B read + 17 B written per unit), on 1 GiB
+    streams (the sustained rate, launch costs amortised), the per-launch floor
+    of a one-wave pass, and a torch device-to-device copy of 1 GiB."""
+    from mxfp4_activation_quantizer_amd import kq
+    stream = torch.cuda.current_stream(dev)
+
+    def ev(call, n, warm):
+        for i in range(warm):
+            call(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms per launch
+
+    def chk(st):
+        if st != 0:
+            raise kq.KQError("kq_stream_ceiling", st)
+
+    R = len(xs)
+    out = {}
+    one = torch.empty(64 * 64, dtype=torch.uint8, device=dev)
+    ms = ev(lambda i: chk(L.kq_stream_ceiling(xs[i % R].data_ptr(), 64, None, one.data_ptr(), sp)),
+            steps, warmup)
+    out["one_wave_pass_host_issued_us"] = round(ms * 1e3, 3)
+    ms = graph_ms(torch, lambda i, st: chk(L.kq_stream_ceiling(xs[i % R].data_ptr(), 64, None,
+                                                        one.data_ptr(), st)), 100)
+    out["launch_floor_graph_us"] = round(ms * 1e3, 3)
+    rbytes, wbytes = units * 64, units * 17
+    ms = ev(lambda i: chk(L.kq_stream_ceiling(xs[i % R].data_ptr(), units, None,
+                                              scales[i % R].data_ptr(), sp)), steps, warmup)
+    out["workload_read_only"] = {"ms_per_step": round(ms, 6),
+                                 "GBps": round(rbytes / (ms * 1e-3) / 1e9, 1)}
+    ms = ev(lambda i: chk(L.kq_stream_ceiling(xs[i % R].data_ptr(), units, codes[i % R].data_ptr(),
+                                              scales[i % R].data_ptr(), sp)), steps, warmup)
+    out["workload_read_write"] = {"ms_per_step": round(ms, 6),
+                                  "GBps": round((rbytes + wbytes) / (ms * 1e-3) / 1e9, 1)}
+    ms = graph_ms(torch, lambda i, st: chk(L.kq_stream_ceiling(xs[i % R].data_ptr(), units,
+                                                        codes[i % R].data_ptr(),
+                                                        scales[i % R].data_ptr(), st)), 4 * R)
+    out["workload_read_write_graph"] = {"ms_per_step": round(ms, 6),
+                                        "GBps": round((rbytes + wbytes) / (ms * 1e-3) / 1e9, 1)}
+    gib = 1 << 30
+    src = torch.empty(gib, dtype=torch.uint8, device=dev)
+    src.fill_(0x3C)
+    gu = gib // 64
+    gc = torch.empty(gu * 16, dtype=torch.uint8, device=dev)
+    gs = torch.empty(gu, dtype=torch.uint8, device=dev)
+    n = max(10, steps // 10)
+    ms = ev(lambda i: chk(L.kq_stream_ceiling(src.data_ptr(), gu, None, gs.data_ptr(), sp)), n, 3)
+    g = gib / (ms * 1e-3) / 1e9
+    out["gib_read_only"] = {"ms_per_step": round(ms, 6), "GBps": round(g, 1),
+                            "frac_of_hbm_peak": round(g / PEAK_HBM_GBS, 4)}
+    ms = ev(lambda i: chk(L.kq_stream_ceiling(src.data_ptr(), gu, gc.data_ptr(), gs.data_ptr(), sp)),
+            n, 3)
+    g = gu * 81 / (ms * 1e-3) / 1e9
+    out["gib_read_write_64_17"] = {"ms_per_step": round(ms, 6), "GBps": round(g, 1),
+                                   "frac_of_hbm_peak": round(g / PEAK_HBM_GBS, 4)}
+    del gc, gs
+    dst = torch.empty_like(src)
+    ms = ev(lambda i: dst.copy_(src), n, 3)
+    g = 2 * gib / (ms * 1e-3) / 1e9
+    out["torch_copy_gib"] = {"ms_per_step": round(ms, 6), "GBps_read_plus_write": round(g, 1),
+                             "frac_of_hbm_peak": round(g / PEAK_HBM_GBS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,11 +488,15 @@ def main() -> int:
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the timed steps of one kernel (for profilers)")
     ap.add_argument("--kernel", default="kq_transform_quant",
-                    choices=["kq_transform_quant", "kq_transform_quant_mfma", "kq_smooth_quant",
-                             "kq_fwht32_quant", "kq_copy_ceiling", "kq_dequant_inverse",
+                    choices=["kq_transform_quant", "kq_transform_quant_mfma",
+                             "kq_transform_quant_quad", "kq_smooth_quant",
+                             "kq_fwht32_quant", "kq_copy_ceiling", "kq_stream_ceiling",
+                             "kq_dequant_inverse",
                              "kq_weight_quant", "kq_w4a4_gemm", "kq_adaln_transform_quant",
                              "kq_adaln_unfused"],
                     help="the entry point --kernel-only times")
+    ap.add_argument("--json-out", metavar="PATH",
+                    help="also write the JSON line to PATH")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise rocprofv3 CSV outputs under DIR into profiles/ and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -351,9 +507,9 @@ def main() -> int:
     if args.summarize_profiles:
         return summarize_profiles(args.summarize_profiles, args.workload)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(token rows shard with no exchange; see the design notes). "
-              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py measures one GPU: token rows and channel blocks are independent, so "
+              f"the quantizer shards with no exchange and one GPU's figure is the per-GPU "
+              f"figure; --gpus {args.gpus} is not supported.", file=sys.stderr)
         return 2
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if world != 1:
@@ -457,8 +613,12 @@ def main() -> int:
                      gemm["wc"].data_ptr(), gemm["ws"].data_ptr(), sp)]
         for i in range(R):
             xp, cp, scp = xs[i].data_ptr(), codes[i].data_ptr(), scales[i].data_ptr()
-            if fn_name in ("kq_transform_quant", "kq_transform_quant_mfma"):
+            if fn_name in ("kq_transform_quant", "kq_transform_quant_mfma",
+                           "kq_transform_quant_quad"):
                 out.append((xp, T, d, d, lu_d.data_ptr(), cp, scp, sp))
+            elif fn_name == "kq_stream_ceiling":
+                # the same bytes as one quantizer step: T * nb units of 64 B
+                out.append((xp, T * nb, cp, scp, sp))
             elif fn_name == "kq_dequant_inverse":
                 # codes/scales of set i back to the bf16 buffer of set i
                 out.append((cp, scp, T, d, lu_d.data_ptr(), xp, d, sp))
@@ -543,6 +703,7 @@ def main() -> int:
     extra = {}
     if not args.no_peers:
         for name, fn_name in [("transform_quant_mfma", "kq_transform_quant_mfma"),
+                              ("transform_quant_quad", "kq_transform_quant_quad"),
                               ("smooth_quant", "kq_smooth_quant"),
                               ("fwht32_quant", "kq_fwht32_quant"),
                               ("copy_ceiling", "kq_copy_ceiling"),
@@ -552,6 +713,14 @@ def main() -> int:
             extra[name] = {"ms_per_step": round(pms, 6), "GBps": round(pg, 1),
                            "frac_of_hbm_peak": round(pg / PEAK_HBM_GBS, 4)}
         extra["frac_of_copy_ceiling"] = round(extra["copy_ceiling"]["ms_per_step"] / ms, 4)
+        gms = graph_ms(torch, lambda i, st: L.kq_transform_quant(
+            xs[i % R].data_ptr(), T, d, d, lu_d.data_ptr(), codes[i % R].data_ptr(),
+            scales[i % R].data_ptr(), st), 4 * R)
+        extra["transform_quant_graph_replay"] = {
+            "ms_per_step": round(gms, 6), "GBps": round(nbytes / (gms * 1e-3) / 1e9, 1),
+            "note": "the same steps captured in one HIP graph and replayed; not the value"}
+        extra["hbm_ceiling"] = hbm_ceilings(L, torch, dev, sp, xs, codes, scales, T * nb,
+                                            args.steps, args.warmup)
         wms = timed_one_set("kq_transform_quant", args.steps, args.warmup)
         extra["mall_warm_single_buffer"] = {
             "ms_per_step": round(wms, 6), "GBps": round(nbytes / (wms * 1e-3) / 1e9, 1),
@@ -573,13 +742,14 @@ def main() -> int:
             extra["adaln_unfused"] = {"ms_per_step": round(ums, 6),
                                       "GBps_moved": round((nbytes + 4 * T * d) / (ums * 1e-3) / 1e9, 1),
                                       "fused_speedup": round(ums / fms, 3)}
-    if not args.no_peers and d == 3072:
+    if not args.no_peers:
         # Calibration of the block parameters from the Hadamard start (per-block
         # (1+1)-ES on the MXFP4 round-trip objective): 150 iterations on 256
         # rows, then the round-trip error on 256 held-out rows.
         xa = inputs.activation(args.workload)
         cal = torch.from_numpy(xa[:256].view(np.int16)).view(torch.bfloat16).to(dev)
-        held = torch.from_numpy(xa[2048:2304].view(np.int16)).view(torch.bfloat16).to(dev)
+        held_rows = slice(2048, 2304)
+        held = torch.from_numpy(xa[held_rows].view(np.int16)).view(torch.bfloat16).to(dev)
         start = torch.from_numpy(inputs.hadamard_init(nb)).to(dev)
         noise = torch.from_numpy(inputs.calib_noise(args.workload, 150)).to(dev)
         kq.calibrate(cal, start, noise[:3])  # warm
@@ -590,7 +760,7 @@ def main() -> int:
         theta, _, _ = kq.calibrate(cal, start, noise)
         c1.record(stream)
         torch.cuda.synchronize()
-        xh = inputs.bf16_bits_to_f32(xa[2048:2304]).astype(np.float64)
+        xh = inputs.bf16_bits_to_f32(xa[held_rows]).astype(np.float64)
         energy = float((xh ** 2).sum())
         f0 = kq.calib_objective(held, start).double().sum().item()
         f1 = kq.calib_objective(held, theta).double().sum().item()
@@ -599,6 +769,8 @@ def main() -> int:
             "ms_per_iteration": round(c0.elapsed_time(c1) / 150, 4),
             "held_out_rel_err_hadamard": round((f0 / energy) ** 0.5, 5),
             "held_out_rel_err_calibrated": round((f1 / energy) ** 0.5, 5)}
+        extra["round_trip_rel_err"] = round_trip_errors(kq, torch, inputs, np, held, xh, lu_d,
+                                                        start, theta, xa)
         if gemm:
             gemm["theta"] = theta
     if gemm:
@@ -645,6 +817,16 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": nbytes}
+    hc = extra.get("hbm_ceiling")
+    if hc:
+        # the same fraction against what was measured in this run: the
+        # streaming reference at this size (launch costs included) and on a
+        # 1 GiB stream (the sustained rate for this read:write mix)
+        roofline["measured_ceiling_same_size_GBps"] = hc["workload_read_write"]["GBps"]
+        roofline["frac_of_measured_ceiling_same_size"] = round(
+            gbs / hc["workload_read_write"]["GBps"], 4)
+        roofline["measured_ceiling_1gib_GBps"] = hc["gib_read_write_64_17"]["GBps"]
+        roofline["frac_of_measured_ceiling_1gib"] = round(gbs / hc["gib_read_write_64_17"]["GBps"], 4)
 
     cpu = None
     if not args.no_cpu:
@@ -684,7 +866,7 @@ def main() -> int:
             cpu["peers"] = oracle_peer_times(oracle, args.workload, x_bits, lu, mult, cores)
 
     line = {
-        "metric": "fused Kron-transform+MXFP4 quantize GB/s & % HBM peak, 4608x3072 bf16, 1 GPU",
+        "metric": f"fused Kron-transform+MXFP4 quantize GB/s & % HBM peak, {T}x{d} bf16, 1 GPU",
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -707,6 +889,9 @@ def main() -> int:
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line), flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(json.dumps(line) + "\n")
     return 0
 
 
