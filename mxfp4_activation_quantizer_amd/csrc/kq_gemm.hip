@@ -64,6 +64,7 @@
 #include "kq.h"
 #include "kq_device.h"
 #include "kq_host.h"
+#include "kq_gemm_wide.h"
 
 namespace kq {
 
@@ -74,6 +75,10 @@ namespace kq {
 #endif
 #ifndef KQ_GEMM_PIPE
 #define KQ_GEMM_PIPE 1
+#endif
+// -DKQ_GEMM_WIDE=0 keeps large problems off the 256 x 256-tile kernel.
+#ifndef KQ_GEMM_WIDE
+#define KQ_GEMM_WIDE 0
 #endif
 static_assert(KQ_GEMM_WPX >= 0, "KQ_GEMM_WPX must be >= 0");
 
@@ -661,6 +666,19 @@ static kq_status launch_gemm(const uint8_t *ac, const uint8_t *as, const uint8_t
             return KQ_ERR_HIP;
         wpx = wpx_env > 0 ? wpx_env : (cus / 8 > 0 ? cus / 8 : 1);
         if (dev >= 0 && dev < 64) wpx_dev[dev].store(wpx, std::memory_order_relaxed);
+    }
+    // Large problems with K a multiple of 256 take the 256 x 256-tile kernel
+    // (less LDS traffic per MFMA); it needs a few tiles per compute unit to
+    // fill the chip.
+    if (KQ_GEMM_WIDE && K % 256 == 0 &&
+        (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 2 * 8 * wpx) {
+        static const bool wide_ok = [] {
+            hipFuncAttributes fa;
+            return hipFuncGetAttributes(&fa, (const void *)wide_kernel_symbol()) == hipSuccess &&
+                   fa.localSizeBytes == 0;
+        }();
+        if (!wide_ok) return KQ_ERR_HIP;
+        return launch_gemm_wide(ac, as, wc, ws, y, M, N, K, ldy, 8 * wpx, stream);
     }
     const int64_t per = (tiles + 7) / 8;
     const int64_t grid = 8 * (per < wpx ? per : wpx);

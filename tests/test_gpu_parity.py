@@ -949,3 +949,41 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
     _log("W4A4 end-to-end rel. error vs X W^T: " +
          ", ".join(f"{k} {v:.4f}" for k, v in errs.items()))
     assert all(v < 0.5 for v in errs.values())
+
+
+# --------------------------------------------------------------------------
+# the 256 x 256-tile kernel: problems with K a multiple of 256 and at least
+# two such tiles per compute unit (a 4608 x 12288 output and larger) take it
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,pad", [(4100, 8200, 1280, 0),   # ragged tiles, 5 K tiles of 256
+                                       (4097, 8193, 256, 24),   # one K tile, strided output
+                                       (4160, 8448, 512, 0),    # two K tiles
+                                       (4352, 8192, 768, 8),    # three K tiles
+                                       (4096, 9000, 2304, 0),   # nine K tiles
+                                       (4608, 12288, 3072, 0),
+                                       # K % 256 == 128: the 128 x 256-tile kernels
+                                       (4100, 8200, 1152, 0)])
+def test_gemm_wide_tiles_random_mxfp4(torch_cuda, M, N, K, pad):
+    torch = torch_cuda
+    g = np.random.default_rng(M + N + K)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    # scale arrays placed 4 bytes past a 16-byte boundary (the ABI's minimum)
+    asb = torch.empty(as_.size + 16, dtype=torch.uint8, device="cuda:0")
+    wsb = torch.empty(ws.size + 16, dtype=torch.uint8, device="cuda:0")
+    asd = asb[4:4 + as_.size].view(M, K // 32)
+    wsd = wsb[4:4 + ws.size].view(N, K // 32)
+    asd.copy_(torch.from_numpy(as_))
+    wsd.copy_(torch.from_numpy(ws))
+    ld = (N + 7) // 8 * 8 + pad  # rows 16-byte aligned
+    ybuf = torch.full((M, ld), -7.0, dtype=torch.bfloat16, device="cuda:0")
+    y = ybuf[:, :N]
+    kq.w4a4_gemm(to_gpu(ac), asd, to_gpu(wc), wsd, y=y)
+    yb = _np(ybuf.view(torch.int16)).view(np.uint16)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 2, M - 1],
+                                     np.random.default_rng(5).choice(M, 6, replace=False)]))
+    _log(f"wide GEMM {M}x{N}x{K}: oracle on {len(rows)} rows")
+    Y, B = gemm_reference(ac[rows], as_[rows], wc, ws)
+    assert_gemm_close(yb[rows, :N], Y, B, K)
+    if ld > N:
+        assert (inputs.bf16_bits_to_f32(yb[:, N:]) == -7.0).all()
