@@ -78,7 +78,7 @@ namespace kq {
 #endif
 // -DKQ_GEMM_WIDE=0 keeps large problems off the 256 x 256-tile kernel.
 #ifndef KQ_GEMM_WIDE
-#define KQ_GEMM_WIDE 0
+#define KQ_GEMM_WIDE 1
 #endif
 static_assert(KQ_GEMM_WPX >= 0, "KQ_GEMM_WPX must be >= 0");
 

@@ -12,23 +12,27 @@
 // K step a wave reads 8 fragments for 16 MFMAs, and per K element the tile
 // fetches 512 rows for 65536 outputs instead of 384 for 32768.
 //
-// K runs in tiles of 256 (128 code bytes and 8 scale bytes per row, whole
-// cache lines per DMA) through two LDS stages of 68 KB: one K tile is in
-// flight while the other is multiplied.  A stage holds A and W codes, 256
-// rows x 128 bytes each, and their scale bytes as two arrays of 4-byte words
-// (low and high half of each row's 8 bytes).  A code row is eight 16-byte
-// chunks at slot c ^ ((row >> 1) & 7): the 16 lanes an LDS cycle serves read
-// 16 consecutive rows at one chunk and so cover all 64 banks once.  A DMA
-// lane writes 16 bytes at (region base + 16 lane), so the layout is made on
-// the global side: the lane landing in slot s of a row fetches chunk
-// s ^ ((row >> 1) & 7).  Scale words are fetched with 4-byte DMAs, one row
-// per lane.
+// K runs in tiles of 256 (128 code bytes per row, whole cache lines per
+// DMA) through two LDS stages of 64 KB: one K tile is in flight while the
+// other is multiplied.  A stage holds A and W codes, 256 rows x 128 bytes
+// each.  A code row is eight 16-byte chunks at slot c ^ ((row >> 1) & 7):
+// the 16 lanes an LDS cycle serves read 16 consecutive rows at one chunk
+// and so cover all 64 banks once.  A DMA lane writes 16 bytes at
+// (region base + 16 lane), so the layout is made on the global side: the
+// lane landing in slot s of a row fetches chunk s ^ ((row >> 1) & 7).
 //
-// Per K tile: wait for this wave's DMAs of the tile (explicit vmcnt), barrier
-// (every wave's DMAs of the tile have landed, and every wave has finished
-// reading the previous tile), issue the DMAs of the next K tile into the
-// other stage, then four K steps of 16 MFMAs.  The DMAs are written as
-// inline assembly and the waits are explicit (see dma16).
+// Scale bytes come in chunks of four K tiles (32 bytes per row, 8 lanes of
+// 4 bytes per row, so a DMA reads 8 rows' contiguous bytes) into two 16 KB
+// buffers; a quarter of the next chunk is fetched during each K tile.  One
+// 4-byte DMA per row and K tile, the first form, touched a separate cache
+// line per lane and made half of all L2 requests.
+//
+// Per K tile: wait for this wave's DMAs (explicit vmcnt), barrier (every
+// wave's DMAs of the tile have landed, and every wave has finished reading
+// the previous tile), then four K steps of 16 MFMAs with the 20 DMAs of the
+// next K tile issued one at a time between the MFMAs of the first three
+// steps.  The DMAs are written as inline assembly and the waits are
+// explicit (see dma16).
 //
 // Epilogue: the bf16 tile (128 KB) goes through the two stages (128 rows
 // each, 8-byte slots at (column / 4) ^ (row & 31)), then every wave stores
@@ -38,6 +42,8 @@
 // for each N tile (as in kq_gemm.hip).
 
 #include <stdint.h>
+
+#include <utility>
 
 #include <hip/hip_runtime.h>
 
@@ -59,15 +65,18 @@ constexpr int kBK = 256;                 // K elements per stage
 constexpr int kRow = kBK / 2;            // 128 code bytes per row per stage
 constexpr int kCodesA = kBM * kRow;      // 32768
 constexpr int kCodesW = kBN * kRow;      // 32768
-constexpr int kScA = kCodesA + kCodesW;  // scale words of A rows: [2][kBM] (low, high 4 bytes)
-constexpr int kScW = kScA + 8 * kBM;     // scale words of W rows: [2][kBN]
-constexpr int kStage = kScW + 8 * kBN;   // 69632 bytes
+constexpr int kStage = kCodesA + kCodesW;  // 65536 code bytes per stage
+constexpr int kChunkKT = 4;                // K tiles per scale chunk
+constexpr int kSRow = 8 * kChunkKT;        // 32 scale bytes per row per chunk
+constexpr int kSBuf = (kBM + kBN) * kSRow; // 16384: A rows, then W rows
 constexpr int kMGroup = 8;
-static_assert(2 * kStage <= 160 * 1024, "two stages fit the LDS");
+static_assert(2 * kStage + 2 * kSBuf <= 160 * 1024, "two stages and two scale chunks fit the LDS");
 static_assert(128 * 512 <= kStage, "128 output rows of bf16 fit one stage");
 
 __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
 __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
+__shared__ __attribute__((aligned(16))) uint8_t sc0[kSBuf];
+__shared__ __attribute__((aligned(16))) uint8_t sc1[kSBuf];
 
 // s_waitcnt vmcnt(n), no expcnt / lgkmcnt wait (gfx9 encoding)
 #define KQW_WAIT_VM(n) \
@@ -77,9 +86,9 @@ __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
 // into one stage made the compiler's wait insertion retire every DMA in
 // flight before the next LDS read; so they are issued here and the waits are
 // explicit.  They are buffer loads: the operand's bounds (num_records) make
-// rows past M or N read as zeros, so a lane needs one offset register per
-// operand (the row step of each DMA and the K tile go into the scalar
-// offset) and no clamping.  M0 holds the LDS base (lane l writes at
+// rows past M or N read as zeros with no clamping (the range check applies
+// to the lane offset, which therefore carries the row; see Plan).  M0 holds
+// the LDS base (lane l writes at
 // M0 + size * l); one wait state separates the write of M0 from the DMA.
 // The compiler reserves M0 and does not preserve it around inline assembly
 // (hence its warning, silenced here): this is sound only while nothing else
@@ -122,15 +131,19 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *l) {
     return (uint32_t)(uintptr_t)(lds_void *)l;
 }
 
-// This lane's DMA sources for one output tile: byte offsets at K tile 0 of
-// its first code chunk in A and W (DMA q adds 32 q rows, in the scalar
-// offset) and of its scale rows.  Every operand is under 2 GiB; rows past
-// the operand's end read zeros.
+// This lane's DMA sources for one output tile, as byte offsets at K 0: of
+// its first code chunk in A and W (DMA q is 32 q rows further) and of its
+// first scale word (8 lanes per row; DMA i of a part is 8 i rows further).
+// The buffer range check sees the lane offset (not the scalar offset), so
+// every row step goes into the lane offset and the scalar offset holds only
+// a position inside the row: rows past the operand's end read zeros and no
+// DMA reads past it.  Every operand is under 2 GiB.
 struct Plan {
     uint32_t va, vw;    // code offsets (A, W)
     uint32_t sa, sw;    // scale offsets (A, W)
     i32x4 ra, rw, rsa, rsw;
     uint32_t row32;     // bytes of 32 code rows
+    uint32_t srow8;     // bytes of 8 scale rows
 };
 
 __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uint8_t *as,
@@ -143,31 +156,85 @@ __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uin
     const uint32_t c16 = 16 * ((lane & 7) ^ ((r0 >> 1) & 7));
     pl.va = (uint32_t)(m0 + r0) * (uint32_t)K2 + c16;
     pl.vw = (uint32_t)(n0 + r0) * (uint32_t)K2 + c16;
-    const int row = wave * 64 + lane;
-    pl.sa = (uint32_t)(m0 + row) * (uint32_t)K32;
-    pl.sw = (uint32_t)(n0 + row) * (uint32_t)K32;
+    const int srow = wave * 32 + (lane >> 3);
+    pl.sa = (uint32_t)(m0 + srow) * (uint32_t)K32 + 4 * (lane & 7);
+    pl.sw = (uint32_t)(n0 + srow) * (uint32_t)K32 + 4 * (lane & 7);
     pl.ra = buffer_rsrc(ac, (uint32_t)M * (uint32_t)K2);
     pl.rw = buffer_rsrc(wc, (uint32_t)N * (uint32_t)K2);
     pl.rsa = buffer_rsrc(as, (uint32_t)M * (uint32_t)K32);
     pl.rsw = buffer_rsrc(ws, (uint32_t)N * (uint32_t)K32);
     pl.row32 = __builtin_amdgcn_readfirstlane(32 * K2);
+    pl.srow8 = __builtin_amdgcn_readfirstlane(8 * K32);
 }
 
-// K tile kt of both operands into stage st.
-__device__ __forceinline__ void issue(const Plan &pl, int kt, int wave, uint8_t *__restrict__ st) {
-    const uint32_t ko = (uint32_t)kt * kRow;
+// The 20 DMAs a wave issues during K tile kt: D = 0 .. 15 are the code rows
+// of K tile kt + 1 (A for even D, W for odd D, 32 (D / 2) rows further
+// down), D = 16 .. 19 a quarter of the scale chunk after the current one:
+// chunk c covers K tiles 4c .. 4c + 3 (32 bytes per row), and during K tile
+// kt, part kt % 4 of chunk kt / 4 + 1 is fetched, 128 rows (rows 0 .. 255 of
+// A for parts 0 and 1, of W for parts 2 and 3), 32 per wave, 8 per DMA.  An
+// empty resource (num_records 0) turns every DMA it serves into zeros
+// written to the LDS with no memory read (past the last K tile or chunk).
+struct Dma {
+    i32x4 ra, rw, rs;
+    uint32_t va, vw, vs, row32, srow8, ko;
+    uint32_t st, ss;  // LDS: this wave's first code region, its scale rows
+};
+
+__device__ __forceinline__ i32x4 with_records(const i32x4 &r, bool live) {
+    return i32x4{r[0], r[1], r[2] & (live ? -1 : 0), r[3]};
+}
+
+__device__ __forceinline__ void make_dma(Dma &dm, const Plan &pl, int kt, int KT, int wave,
+                                         uint8_t *__restrict__ st) {
+    const bool live = kt + 1 < KT;
+    dm.ra = with_records(pl.ra, live);
+    dm.rw = with_records(pl.rw, live);
+    dm.va = pl.va;
+    dm.vw = pl.vw;
+    dm.row32 = pl.row32;
+    dm.srow8 = pl.srow8;
+    dm.ko = __builtin_amdgcn_readfirstlane((uint32_t)(kt + 1) * kRow);
+    dm.st = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024);
+    const int chunk = (kt >> 2) + 1, part = kt & 3;
+    dm.rs = with_records(part < 2 ? pl.rsa : pl.rsw, chunk * kChunkKT < KT);
+    dm.vs = (part < 2 ? pl.sa : pl.sw) + (uint32_t)chunk * kSRow + (uint32_t)(part & 1) * 16 * pl.srow8;
+    dm.ss = __builtin_amdgcn_readfirstlane(lds_addr(chunk & 1 ? sc1 : sc0) +
+                                           (part * 128 + wave * 32) * kSRow);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_one(const Dma &dm) {
+    if constexpr (D < 16) {
+        constexpr int q = D >> 1;
+        // region q * 4 + wave of 1 KB
+        if constexpr ((D & 1) == 0)
+            dma16(dm.ra, dm.va + q * dm.row32, dm.ko, dm.st + q * 4096);
+        else
+            dma16(dm.rw, dm.vw + q * dm.row32, dm.ko, dm.st + kCodesA + q * 4096);
+    } else {
+        constexpr int i = D - 16;
+        dma4(dm.rs, dm.vs + i * dm.srow8, 0, dm.ss + i * 8 * kSRow);
+    }
+}
+
+// The first K tile of an output tile into stage 0 and the whole first scale
+// chunk into its buffer, all at once.
+__device__ __forceinline__ void issue_first(const Plan &pl, int wave) {
+    const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(st0) + wave * 1024);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const uint32_t so = __builtin_amdgcn_readfirstlane(ko + q * pl.row32);
-        dma16(pl.ra, pl.va, so, lds_addr(st + (q * 4 + wave) * 1024));
-        dma16(pl.rw, pl.vw, so, lds_addr(st + kCodesA + (q * 4 + wave) * 1024));
+        dma16(pl.ra, pl.va + q * pl.row32, 0, st + q * 4096);
+        dma16(pl.rw, pl.vw + q * pl.row32, 0, st + kCodesA + q * 4096);
     }
-    // a row's 8 scale bytes: low and high 4-byte words into two arrays
-    const uint32_t s0 = __builtin_amdgcn_readfirstlane(kt * 8), s1 = s0 + 4;
-    dma4(pl.rsa, pl.sa, s0, lds_addr(st + kScA + wave * 256));
-    dma4(pl.rsa, pl.sa, s1, lds_addr(st + kScA + 4 * kBM + wave * 256));
-    dma4(pl.rsw, pl.sw, s0, lds_addr(st + kScW + wave * 256));
-    dma4(pl.rsw, pl.sw, s1, lds_addr(st + kScW + 4 * kBN + wave * 256));
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_addr(sc0) + (part * 128 + wave * 32) * kSRow);
+        const uint32_t vs = (part < 2 ? pl.sa : pl.sw) + (uint32_t)(part & 1) * 16 * pl.srow8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma4(part < 2 ? pl.rsa : pl.rsw, vs + i * pl.srow8, 0, ss + i * 8 * kSRow);
+    }
 }
 
 __device__ __forceinline__ i32x8 frag(const uint8_t *b, int row, int ch) {
@@ -191,18 +258,45 @@ __device__ __forceinline__ void load_frags(const uint8_t *__restrict__ b, int wm
     for (int i = 0; i < 4; ++i) f.w[i] = frag(b + kCodesA, wn * 128 + i * 32 + i32, ch);
 }
 
-// The 16 MFMAs of K step KS; its scale byte is byte 2 (KS % 2) of word KS / 2
-// (see compute).
+// The DMA issued after MFMA m of K step ks, or -1: the 16 code DMAs after
+// the odd MFMAs of steps 0 and 1, the 4 scale DMAs in step 2.  Spread out so
+// that the wave never waits long to hand a DMA over while its MFMAs could
+// issue; issued all at once after the barrier, they held the matrix cores
+// idle for a good part of every K tile.
+constexpr int dma_after(int ks, int m) {
+    return ks < 2 ? ((m & 1) ? ks * 8 + (m >> 1) : -1)
+                  : (ks == 2 && (m & 3) == 3 ? 16 + (m >> 2) : -1);
+}
+
+// MFMA m = 4 i + j of K step KS (its scale byte is byte 2 (KS % 2) of word
+// KS / 2, see compute), then its DMA if it has one; the scheduling barriers
+// keep the DMA where it is placed.
+template <int KS, int MI>
+__device__ __forceinline__ void mfma_one(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
+                                         f32x16 (&acc)[4][4], const Dma &dm) {
+    constexpr int kSel = 2 * (KS & 1), kWord = KS >> 1, i = MI >> 2, j = MI & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        f.w[i], f.a[j], acc[i][j], 4, 4, kSel, (int)sw[i][kWord], kSel, (int)sa[j][kWord]);
+    constexpr int d = dma_after(KS, MI);
+    if constexpr (d >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one<d>(dm);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int KS, int... MI>
+__device__ __forceinline__ void mfma_seq(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
+                                         f32x16 (&acc)[4][4], const Dma &dm,
+                                         std::integer_sequence<int, MI...>) {
+    (mfma_one<KS, MI>(f, sa, sw, acc, dm), ...);
+}
+
+// The 16 MFMAs of K step KS, with their share of the next K tile's DMAs.
 template <int KS>
 __device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
-                                       f32x16 (&acc)[4][4]) {
-    constexpr int kSel = 2 * (KS & 1), kWord = KS >> 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                f.w[i], f.a[j], acc[i][j], 4, 4, kSel, (int)sw[i][kWord], kSel, (int)sa[j][kWord]);
+                                       f32x16 (&acc)[4][4], const Dma &dm) {
+    mfma_seq<KS>(f, sa, sw, acc, dm, std::make_integer_sequence<int, 16>{});
 }
 
 // The four K steps of stage b.  A row's 8 scale bytes (the stage's eight
@@ -213,36 +307,36 @@ __device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], con
 // scheduling barriers keep it to two fragment sets in registers (left free,
 // the compiler read all four steps' fragments ahead and ran out of
 // registers).
-__device__ __forceinline__ void compute(const uint8_t *__restrict__ b, int wm, int wn, int i32, int kg,
-                                        f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void compute(const uint8_t *__restrict__ b, const uint8_t *__restrict__ sc,
+                                        int wm, int wn, int i32, int kg, f32x16 (&acc)[4][4],
+                                        const Dma &dm) {
+    // sc: this K tile's 8 scale bytes of every row (row stride kSRow)
     u32x2 sa[4], sw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + i32;
-        const uint64_t v = ((uint64_t)*reinterpret_cast<const uint32_t *>(b + kScA + 4 * kBM + 4 * r) << 32 |
-                            *reinterpret_cast<const uint32_t *>(b + kScA + 4 * r)) >> (8 * kg);
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow) >> (8 * kg);
         sa[j] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wn * 128 + i * 32 + i32;
-        const uint64_t v = ((uint64_t)*reinterpret_cast<const uint32_t *>(b + kScW + 4 * kBN + 4 * r) << 32 |
-                            *reinterpret_cast<const uint32_t *>(b + kScW + 4 * r)) >> (8 * kg);
+        const int r = kBM + wn * 128 + i * 32 + i32;
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow) >> (8 * kg);
         sw[i] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
     Frags f0, f1;
     load_frags<0>(b, wm, wn, i32, kg, f0);
     __builtin_amdgcn_sched_barrier(0);
     load_frags<1>(b, wm, wn, i32, kg, f1);
-    mfma16<0>(f0, sa, sw, acc);
+    mfma16<0>(f0, sa, sw, acc, dm);
     __builtin_amdgcn_sched_barrier(0);
     load_frags<2>(b, wm, wn, i32, kg, f0);
-    mfma16<1>(f1, sa, sw, acc);
+    mfma16<1>(f1, sa, sw, acc, dm);
     __builtin_amdgcn_sched_barrier(0);
     load_frags<3>(b, wm, wn, i32, kg, f1);
-    mfma16<2>(f0, sa, sw, acc);
+    mfma16<2>(f0, sa, sw, acc, dm);
     __builtin_amdgcn_sched_barrier(0);
-    mfma16<3>(f1, sa, sw, acc);
+    mfma16<3>(f1, sa, sw, acc, dm);
 }
 
 __device__ __forceinline__ void tile_origin(int lin, int mtc, int ntc, int &m0, int &n0) {
@@ -261,11 +355,16 @@ __device__ __forceinline__ void kstep(const Plan &pl, int kt, int KT, int wave, 
     uint8_t *const rd = U == 0 ? st0 : st1;
     uint8_t *const in = U == 0 ? st1 : st0;
     // this wave's DMAs of tile kt have landed (none younger are in flight:
-    // tile kt + 1 is issued below)
+    // tile kt + 1 is issued during compute)
     KQW_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
-    if (kt + 1 < KT) issue(pl, kt + 1, wave, in);
-    compute(rd, wm, wn, i32, kg, acc);
+    // K tile kt + 1 into the other stage and a quarter of the next scale
+    // chunk, or, past the last ones, zeros with no memory read (no branch
+    // around the accumulating steps)
+    Dma dm;
+    make_dma(dm, pl, kt, KT, wave, in);
+    const uint8_t *sc = ((kt >> 2) & 1 ? sc1 : sc0) + (kt & 3) * 8;
+    compute(rd, sc, wm, wn, i32, kg, acc, dm);
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
@@ -285,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
         tile_origin(lin, mtc, ntc, m0, n0);
         Plan pl;
         make_plan(pl, ac, as, wc, ws, m0, n0, M, N, K2, K32, wave, lane);
-        issue(pl, 0, wave, st0);
+        issue_first(pl, wave);
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -303,8 +402,10 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
         }
         if (kt < KT) kstep<0>(pl, kt, KT, wave, wm, wn, i32, kg, acc);
 
-        // ---- epilogue: every wave is done reading the stages; the wait
-        //      states cover the last MFMAs' results before their reads ----
+        // ---- epilogue: the last zero DMAs have landed and every wave is
+        //      done reading the stages; the wait states cover the last
+        //      MFMAs' results before their reads ----
+        KQW_WAIT_VM(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         __builtin_amdgcn_s_barrier();
         const int ekey = kg ^ i32;
