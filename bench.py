@@ -85,6 +85,7 @@ KERNEL_MATCH = {
 
 PROFILE_COMMANDS = """\
 cd /tmp && export TMPDIR=/tmp; cd $REPO
+python3 bench.py --json-out OUT/bench.json
 rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o trace -- python3 bench.py --steps 200 --warmup 50 --no-cpu
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o FETCH_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/WRITE_SIZE -o WRITE_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
@@ -248,8 +249,54 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                 lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
                              f"{pct(key, 0.5):8.3f} {pct(key, 0.9):8.3f} "
                              f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} {rate}")
+    bench_rec = None
+    bench_path = os.path.join(out_dir, "bench.json")
+    if os.path.exists(bench_path):
+        with open(bench_path) as f:
+            bench_rec = json.loads(f.readline())
+        traced = next((float(r["AverageNs"]) / 1e3 for r in stats
+                       if KERNEL_MATCH["kq_transform_quant"] in r["Name"]), float("nan"))
+        bus = bench_rec["ms_per_step"] * 1e3
+        lines += [f"# bench.py run in the same call (OUT/bench.json): ms_per_step {bus:.3f} us "
+                  f"({bench_rec['value']} GB/s, frac {bench_rec['roofline']['frac']}); traced "
+                  f"kq_transform_quant average {traced:.3f} us = {traced / bus:.3f} x ms_per_step; "
+                  f"frac from the traced average {nbytes / (traced * 1e3) / PEAK_HBM_GBS:.4f}"]
     with open(os.path.join(PROFILES, f"kernel_stats_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    hc = (bench_rec or {}).get("peers", {}).get("hbm_ceiling")
+    if hc:
+        frac = bench_rec["roofline"]["frac"]
+        gbs = bench_rec["value"]
+        hl = [f"# HBM ceilings measured by bench.py ({workload} {w.tokens}x{w.d}) with "
+              f"kq_stream_ceiling: wave-contiguous 16-byte loads, no arithmetic, a lane mapping of",
+              "# its own (not the quantizer's); 1 GiB streams amortise launch costs; the 64:17 mix is",
+              "# the quantizer's bytes per 32-element unit (64 read, 16 + 1 written)",
+              f"# kernel sources {src_hash}; command: python3 bench.py --json-out OUT/bench.json"
+              + (f" --workload {workload}" if workload != "flux_attn" else ""),
+              f"{'stream':44s} {'us':>10s} {'GB/s':>9s} {'of 8 TB/s':>9s}"]
+        for key, label, b in (("gib_read_only", "1 GiB read only", 1 << 30),
+                              ("gib_read_write_64_17", "1 GiB read + 17/64 written", None)):
+            r = hc[key]
+            hl.append(f"{label:44s} {r['ms_per_step'] * 1e3:10.2f} {r['GBps']:9.1f} "
+                      f"{r['GBps'] / PEAK_HBM_GBS:9.4f}")
+        for key, label in (("workload_read_only", f"{w.tokens}x{w.d} size, read only"),
+                           ("workload_read_write", f"{w.tokens}x{w.d} size, 64:17, host-issued"),
+                           ("workload_read_write_graph", f"{w.tokens}x{w.d} size, 64:17, graph replay")):
+            r = hc[key]
+            hl.append(f"{label:44s} {r['ms_per_step'] * 1e3:10.3f} {r['GBps']:9.1f} "
+                      f"{r['GBps'] / PEAK_HBM_GBS:9.4f}")
+        if "torch_copy_gib" in hc:
+            r = hc["torch_copy_gib"]
+            hl.append(f"{'torch device copy of 1 GiB (read + write)':44s} {r['ms_per_step'] * 1e3:10.2f} "
+                      f"{r['GBps_read_plus_write']:9.1f} {r['frac_of_hbm_peak']:9.4f}")
+        hl.append(f"{'one-wave pass, host-issued (launch floor)':44s} {hc['one_wave_pass_host_issued_us']:10.3f}")
+        hl.append(f"{'one-wave pass, graph replay':44s} {hc['launch_floor_graph_us']:10.3f}")
+        hl.append(f"kq_transform_quant in the same run: {gbs} GB/s = frac {frac} of 8 TB/s, "
+                  f"{gbs / hc['gib_read_write_64_17']['GBps']:.4f} of the 1 GiB 64:17 stream, "
+                  f"{gbs / hc['workload_read_write']['GBps']:.4f} of the same-size 64:17 stream")
+        with open(os.path.join(PROFILES, "hbm_ceiling.txt" if workload == "flux_attn"
+                               else f"hbm_ceiling_{workload}.txt"), "w") as f:
+            f.write("\n".join(hl) + "\n")
 
     def counter_avg(sub, counter, match):
         rows = _csv_rows(_find(os.path.join(out_dir, sub), "counter_collection.csv"))

@@ -953,16 +953,19 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
 
 # --------------------------------------------------------------------------
 # the 256 x 256-tile kernel: problems with K a multiple of 256 and at least
-# two such tiles per compute unit (a 4608 x 12288 output and larger) take it
+# two such tiles per compute unit (a 4608 x 12288 output and larger) take it;
+# scales come in chunks of four K tiles of 256
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,K,pad", [(4100, 8200, 1280, 0),   # ragged tiles, 5 K tiles of 256
                                        (4097, 8193, 256, 24),   # one K tile, strided output
                                        (4160, 8448, 512, 0),    # two K tiles
                                        (4352, 8192, 768, 8),    # three K tiles
-                                       (4096, 9000, 2304, 0),   # nine K tiles
+                                       (4160, 8200, 1024, 8),   # one scale chunk exactly
+                                       (4096, 9000, 2304, 0),   # nine K tiles, a partial chunk
                                        (4608, 12288, 3072, 0),
                                        # K % 256 == 128: the 128 x 256-tile kernels
-                                       (4100, 8200, 1152, 0)])
+                                       (4100, 8200, 1152, 0),
+                                       (4097, 8200, 128, 0)])
 def test_gemm_wide_tiles_random_mxfp4(torch_cuda, M, N, K, pad):
     torch = torch_cuda
     g = np.random.default_rng(M + N + K)
