@@ -72,10 +72,11 @@ KERNEL_MATCH = {
     "kq_smooth_quant": "SmoothStage, kq::Mxfp4Sink",
     "kq_fwht32_quant": "FwhtStage, kq::Mxfp4Sink",
     "kq_copy_ceiling": "IdentityStage, kq::FoldSink",
-    "kq_stream_ceiling": "stream_kernel",
+    "kq_stream_ceiling (read + write)": "stream_kernel<true>",
+    "kq_stream_ceiling (read only)": "stream_kernel<false>",
     "kq_dequant_inverse": "KronInverseStage, kq::Bf16Sink",
     "kq_weight_quant": "KronWeightStage, kq::Mxfp4Sink",
-    "kq_w4a4_gemm": "w4a4_gemm_",  # the per-tile and the cross-tile pipelined kernel
+    "kq_w4a4_gemm": ("w4a4_gemm_", "gemm_wide_kernel"),  # per-tile, pipelined, 256 x 256
     "kq_adaln_transform_quant": "adaln_kernel<1, true>",
     "kq_adaln_modulate": "adaln_kernel<1, false>",
     "kq_calib_objective": "calib_objective_kernel",
@@ -182,6 +183,11 @@ def _find(directory, suffix):
     raise FileNotFoundError(f"no *{suffix} under {directory}")
 
 
+def _kmatch(entry: str, name: str) -> bool:
+    keys = KERNEL_MATCH[entry]
+    return any(k in name for k in ((keys,) if isinstance(keys, str) else keys))
+
+
 def profile_commands(workload: str = "flux_attn") -> list:
     """PROFILE_COMMANDS for a workload: the bench runs take --workload when it
     is not the default one (the copy calibration is the same for all)."""
@@ -218,8 +224,8 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
         durations.setdefault(r["Kernel_Name"], []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
-    def pct(name_key, q):
-        vals = sorted(v for k, vs in durations.items() if name_key in k for v in vs)
+    def pct(name, q):
+        vals = sorted(v for k, vs in durations.items() if k == name for v in vs)
         return vals[min(len(vals) - 1, int(q * len(vals)))] if vals else float("nan")
 
     lines = [f"# rocprofv3 --kernel-trace --stats, {workload} {w.tokens}x{w.d} bf16, one MI355X",
@@ -230,12 +236,16 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                  f"{'min us':>8s} {'max us':>8s} {'GB/s(avg)':>10s}")
     gemm_flops = 2.0 * w.tokens * inputs.GEMM_N * inputs.GEMM_K
     weight_bytes = inputs.GEMM_N * inputs.GEMM_K * (2 + 0.5 + 1 / 32)
-    for entry, key in KERNEL_MATCH.items():
+    for entry in KERNEL_MATCH:
         for r in stats:
-            if key in r["Name"]:
+            if _kmatch(entry, r["Name"]):
                 avg = float(r["AverageNs"]) / 1e3
                 if entry == "kq_w4a4_gemm":
-                    rate = f"{gemm_flops / (avg * 1e6):10.1f} TFLOP/s ({w.tokens}x{inputs.GEMM_N}x{inputs.GEMM_K})"
+                    kind = "256 x 256 tiles" if "gemm_wide_kernel" in r["Name"] else "128 x 256 tiles"
+                    rate = (f"{gemm_flops / (avg * 1e6):10.1f} TFLOP/s ({w.tokens}x{inputs.GEMM_N}x"
+                            f"{inputs.GEMM_K}, {kind})")
+                elif entry.startswith("kq_stream_ceiling"):
+                    rate = f"{'':>10s} (workload-size and 1 GiB streams together)"
                 elif entry == "kq_weight_quant":
                     rate = f"{weight_bytes / (avg * 1e3):10.1f} ({inputs.GEMM_N}x{inputs.GEMM_K} weight)"
                 elif entry == "kq_adaln_modulate":
@@ -247,7 +257,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                 else:
                     rate = f"{nbytes / (avg * 1e3):10.1f}"
                 lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
-                             f"{pct(key, 0.5):8.3f} {pct(key, 0.9):8.3f} "
+                             f"{pct(r['Name'], 0.5):8.3f} {pct(r['Name'], 0.9):8.3f} "
                              f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} {rate}")
     bench_rec = None
     bench_path = os.path.join(out_dir, "bench.json")
@@ -353,7 +363,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
         rows = _csv_rows(_find(os.path.join(out_dir, sub), "counter_collection.csv"))
         means = {}
         for r in rows:
-            if KERNEL_MATCH[entry] in r["Kernel_Name"]:
+            if _kmatch(entry, r["Kernel_Name"]):
                 means.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
         means = {k: sum(v) / len(v) for k, v in means.items()}
         ctr.append(f"{entry}:")

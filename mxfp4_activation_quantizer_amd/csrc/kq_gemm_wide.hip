@@ -23,7 +23,10 @@
 //
 // Scale bytes come in chunks of four K tiles (32 bytes per row, 8 lanes of
 // 4 bytes per row, so a DMA reads 8 rows' contiguous bytes) into two 16 KB
-// buffers; a quarter of the next chunk is fetched during each K tile.  One
+// buffers; a quarter of the next chunk is fetched during each K tile.  In
+// the LDS, row r keeps K tile q's 8 bytes at unit q ^ ((r >> 3) & 3) (the
+// DMA lanes fetch their words in that order), so that reading one K tile's
+// bytes of 32 consecutive rows touches every bank once.  One
 // 4-byte DMA per row and K tile, the first form, touched a separate cache
 // line per lane and made half of all L2 requests.
 //
@@ -144,6 +147,7 @@ struct Plan {
     i32x4 ra, rw, rsa, rsw;
     uint32_t row32;     // bytes of 32 code rows
     uint32_t srow8;     // bytes of 8 scale rows
+    uint32_t sword;     // this lane's byte in a row's 32 scale bytes, before the swizzle
 };
 
 __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uint8_t *as,
@@ -157,8 +161,9 @@ __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uin
     pl.va = (uint32_t)(m0 + r0) * (uint32_t)K2 + c16;
     pl.vw = (uint32_t)(n0 + r0) * (uint32_t)K2 + c16;
     const int srow = wave * 32 + (lane >> 3);
-    pl.sa = (uint32_t)(m0 + srow) * (uint32_t)K32 + 4 * (lane & 7);
-    pl.sw = (uint32_t)(n0 + srow) * (uint32_t)K32 + 4 * (lane & 7);
+    pl.sa = (uint32_t)(m0 + srow) * (uint32_t)K32;
+    pl.sw = (uint32_t)(n0 + srow) * (uint32_t)K32;
+    pl.sword = 4 * (lane & 7);
     pl.ra = buffer_rsrc(ac, (uint32_t)M * (uint32_t)K2);
     pl.rw = buffer_rsrc(wc, (uint32_t)N * (uint32_t)K2);
     pl.rsa = buffer_rsrc(as, (uint32_t)M * (uint32_t)K32);
@@ -177,7 +182,7 @@ __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uin
 // written to the LDS with no memory read (past the last K tile or chunk).
 struct Dma {
     i32x4 ra, rw, rs;
-    uint32_t va, vw, vs, row32, srow8, ko;
+    uint32_t va, vw, vs, row32, srow8, ko, sword;
     uint32_t st, ss;  // LDS: this wave's first code region, its scale rows
 };
 
@@ -194,6 +199,7 @@ __device__ __forceinline__ void make_dma(Dma &dm, const Plan &pl, int kt, int KT
     dm.vw = pl.vw;
     dm.row32 = pl.row32;
     dm.srow8 = pl.srow8;
+    dm.sword = pl.sword;
     dm.ko = __builtin_amdgcn_readfirstlane((uint32_t)(kt + 1) * kRow);
     dm.st = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024);
     const int chunk = (kt >> 2) + 1, part = kt & 3;
@@ -214,7 +220,7 @@ __device__ __forceinline__ void issue_one(const Dma &dm) {
             dma16(dm.rw, dm.vw + q * dm.row32, dm.ko, dm.st + kCodesA + q * 4096);
     } else {
         constexpr int i = D - 16;
-        dma4(dm.rs, dm.vs + i * dm.srow8, 0, dm.ss + i * 8 * kSRow);
+        dma4(dm.rs, dm.vs + i * dm.srow8 + (dm.sword ^ (8 * i)), 0, dm.ss + i * 8 * kSRow);
     }
 }
 
@@ -233,7 +239,8 @@ __device__ __forceinline__ void issue_first(const Plan &pl, int wave) {
         const uint32_t vs = (part < 2 ? pl.sa : pl.sw) + (uint32_t)(part & 1) * 16 * pl.srow8;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dma4(part < 2 ? pl.rsa : pl.rsw, vs + i * pl.srow8, 0, ss + i * 8 * kSRow);
+            dma4(part < 2 ? pl.rsa : pl.rsw, vs + i * pl.srow8 + (pl.sword ^ (8 * i)), 0,
+                 ss + i * 8 * kSRow);
     }
 }
 
@@ -308,20 +315,24 @@ __device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], con
 // the compiler read all four steps' fragments ahead and ran out of
 // registers).
 __device__ __forceinline__ void compute(const uint8_t *__restrict__ b, const uint8_t *__restrict__ sc,
-                                        int wm, int wn, int i32, int kg, f32x16 (&acc)[4][4],
+                                        int kq, int wm, int wn, int i32, int kg, f32x16 (&acc)[4][4],
                                         const Dma &dm) {
-    // sc: this K tile's 8 scale bytes of every row (row stride kSRow)
+    // sc: the scale chunk; kq: the K tile within it.  Row r holds its four
+    // K tiles' 8-byte groups at unit q ^ ((r >> 3) & 3) (so that 32
+    // consecutive rows' reads of one K tile cover all banks); every row this
+    // lane reads has (r >> 3) & 3 = (i32 >> 3) & 3.
+    const int sx = 8 * (kq ^ ((i32 >> 3) & 3));
     u32x2 sa[4], sw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + i32;
-        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow) >> (8 * kg);
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow + sx) >> (8 * kg);
         sa[j] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = kBM + wn * 128 + i * 32 + i32;
-        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow) >> (8 * kg);
+        const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow + sx) >> (8 * kg);
         sw[i] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
     Frags f0, f1;
@@ -363,8 +374,7 @@ __device__ __forceinline__ void kstep(const Plan &pl, int kt, int KT, int wave, 
     // around the accumulating steps)
     Dma dm;
     make_dma(dm, pl, kt, KT, wave, in);
-    const uint8_t *sc = ((kt >> 2) & 1 ? sc1 : sc0) + (kt & 3) * 8;
-    compute(rd, sc, wm, wn, i32, kg, acc, dm);
+    compute(rd, (kt >> 2) & 1 ? sc1 : sc0, kt & 3, wm, wn, i32, kg, acc, dm);
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
