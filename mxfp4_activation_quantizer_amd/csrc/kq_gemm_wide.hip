@@ -10,7 +10,9 @@
 // four waves (one per SIMD) computes a 256 x 256 tile, each wave 128 x 128
 // as 4 x 4 MFMA tiles (256 accumulator registers, in the AGPRs): per 64-wide
 // K step a wave reads 8 fragments for 16 MFMAs, and per K element the tile
-// fetches 512 rows for 65536 outputs instead of 384 for 32768.
+// fetches 512 rows for 65536 outputs instead of 384 for 32768.  A build
+// with -DKQ_GEMM_WIDE_WAVES=8 runs eight waves (two per SIMD, 128 x 64
+// each, 128 accumulators): correct, and no faster.
 //
 // K runs in tiles of 256 (128 code bytes per row, whole cache lines per
 // DMA) through two LDS stages of 64 KB: one K tile is in flight while the
@@ -62,7 +64,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 256;            // four waves, one per SIMD
+// Waves per workgroup: 4 (one per SIMD, 128 x 128 each) or 8 (two per
+// SIMD, 128 x 64 each); -DKQ_GEMM_WIDE_WAVES selects it.
+#ifndef KQ_GEMM_WIDE_WAVES
+#define KQ_GEMM_WIDE_WAVES 4
+#endif
+constexpr int kWaves = KQ_GEMM_WIDE_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "KQ_GEMM_WIDE_WAVES must be 4 or 8");
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWN = kWaves / 2;          // wave columns; wave rows: 2
+constexpr int kTI = 256 / kWN / 32;      // 32-column MFMA tiles per wave (4 or 2)
+constexpr int kCodeDma = 64 / kWaves;    // code DMAs per wave per K tile (16 or 8)
+constexpr int kScaleDma = 16 / kWaves;   // scale DMAs per wave per K tile (4 or 2)
 constexpr int kBM = 256, kBN = 256;      // output tile
 constexpr int kBK = 256;                 // K elements per stage
 constexpr int kRow = kBK / 2;            // 128 code bytes per row per stage
@@ -145,7 +158,7 @@ struct Plan {
     uint32_t va, vw;    // code offsets (A, W)
     uint32_t sa, sw;    // scale offsets (A, W)
     i32x4 ra, rw, rsa, rsw;
-    uint32_t row32;     // bytes of 32 code rows
+    uint32_t row32;     // bytes of 8 kWaves code rows (one DMA step)
     uint32_t srow8;     // bytes of 8 scale rows
     uint32_t sword;     // this lane's byte in a row's 32 scale bytes, before the swizzle
 };
@@ -153,14 +166,14 @@ struct Plan {
 __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uint8_t *as,
                                           const uint8_t *wc, const uint8_t *ws, int m0, int n0,
                                           int M, int N, int K2, int K32, int wave, int lane) {
-    // DMA q writes 1 KB region q * 4 + wave: rows (q * 4 + wave) * 8 + lane / 8
-    // (= the lane's row + 32 q), slot lane % 8, which holds chunk
-    // slot ^ ((row >> 1) & 7); row + 32 q has the same low bits
+    // DMA q writes 1 KB region q * kWaves + wave: rows (q * kWaves + wave) * 8
+    // + lane / 8 (= the lane's row + 8 kWaves q), slot lane % 8, which holds
+    // chunk slot ^ ((row >> 1) & 7); row + 8 kWaves q has the same low bits
     const int r0 = wave * 8 + (lane >> 3);
     const uint32_t c16 = 16 * ((lane & 7) ^ ((r0 >> 1) & 7));
     pl.va = (uint32_t)(m0 + r0) * (uint32_t)K2 + c16;
     pl.vw = (uint32_t)(n0 + r0) * (uint32_t)K2 + c16;
-    const int srow = wave * 32 + (lane >> 3);
+    const int srow = wave * (128 / kWaves) + (lane >> 3);
     pl.sa = (uint32_t)(m0 + srow) * (uint32_t)K32;
     pl.sw = (uint32_t)(n0 + srow) * (uint32_t)K32;
     pl.sword = 4 * (lane & 7);
@@ -168,21 +181,22 @@ __device__ __forceinline__ void make_plan(Plan &pl, const uint8_t *ac, const uin
     pl.rw = buffer_rsrc(wc, (uint32_t)N * (uint32_t)K2);
     pl.rsa = buffer_rsrc(as, (uint32_t)M * (uint32_t)K32);
     pl.rsw = buffer_rsrc(ws, (uint32_t)N * (uint32_t)K32);
-    pl.row32 = __builtin_amdgcn_readfirstlane(32 * K2);
+    pl.row32 = __builtin_amdgcn_readfirstlane(8 * kWaves * K2);
     pl.srow8 = __builtin_amdgcn_readfirstlane(8 * K32);
 }
 
-// The 20 DMAs a wave issues during K tile kt: D = 0 .. 15 are the code rows
-// of K tile kt + 1 (A for even D, W for odd D, 32 (D / 2) rows further
-// down), D = 16 .. 19 a quarter of the scale chunk after the current one:
-// chunk c covers K tiles 4c .. 4c + 3 (32 bytes per row), and during K tile
-// kt, part kt % 4 of chunk kt / 4 + 1 is fetched, 128 rows (rows 0 .. 255 of
-// A for parts 0 and 1, of W for parts 2 and 3), 32 per wave, 8 per DMA.  An
-// empty resource (num_records 0) turns every DMA it serves into zeros
-// written to the LDS with no memory read (past the last K tile or chunk).
+// The DMAs a wave issues during K tile kt (20 with four waves, 10 with
+// eight): D < kCodeDma are the code rows of K tile kt + 1 (A for even D, W
+// for odd D, 8 kWaves (D / 2) rows further down), the next kScaleDma a
+// quarter of the scale chunk after the current one: chunk c covers K tiles
+// 4c .. 4c + 3 (32 bytes per row), and during K tile kt, part kt % 4 of
+// chunk kt / 4 + 1 is fetched, 128 rows (rows 0 .. 255 of A for parts 0 and
+// 1, of W for parts 2 and 3), 128 / kWaves per wave, 8 per DMA.  An empty
+// resource (num_records 0) turns every DMA it serves into zeros written to
+// the LDS with no memory read (past the last K tile or chunk).
 struct Dma {
     i32x4 ra, rw, rs;
-    uint32_t va, vw, vs, row32, srow8, ko, sword;
+    uint32_t va, vw, vs, row32, srow8, ko, sword, skey;
     uint32_t st, ss;  // LDS: this wave's first code region, its scale rows
 };
 
@@ -202,25 +216,27 @@ __device__ __forceinline__ void make_dma(Dma &dm, const Plan &pl, int kt, int KT
     dm.sword = pl.sword;
     dm.ko = __builtin_amdgcn_readfirstlane((uint32_t)(kt + 1) * kRow);
     dm.st = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024);
+    dm.skey = (wave * (16 / kWaves)) & 3;
     const int chunk = (kt >> 2) + 1, part = kt & 3;
     dm.rs = with_records(part < 2 ? pl.rsa : pl.rsw, chunk * kChunkKT < KT);
     dm.vs = (part < 2 ? pl.sa : pl.sw) + (uint32_t)chunk * kSRow + (uint32_t)(part & 1) * 16 * pl.srow8;
     dm.ss = __builtin_amdgcn_readfirstlane(lds_addr(chunk & 1 ? sc1 : sc0) +
-                                           (part * 128 + wave * 32) * kSRow);
+                                           (part * 128 + wave * (128 / kWaves)) * kSRow);
 }
 
 template <int D>
 __device__ __forceinline__ void issue_one(const Dma &dm) {
-    if constexpr (D < 16) {
+    if constexpr (D < kCodeDma) {
         constexpr int q = D >> 1;
-        // region q * 4 + wave of 1 KB
+        // region q * kWaves + wave of 1 KB
         if constexpr ((D & 1) == 0)
-            dma16(dm.ra, dm.va + q * dm.row32, dm.ko, dm.st + q * 4096);
+            dma16(dm.ra, dm.va + q * dm.row32, dm.ko, dm.st + q * kWaves * 1024);
         else
-            dma16(dm.rw, dm.vw + q * dm.row32, dm.ko, dm.st + kCodesA + q * 4096);
+            dma16(dm.rw, dm.vw + q * dm.row32, dm.ko, dm.st + kCodesA + q * kWaves * 1024);
     } else {
-        constexpr int i = D - 16;
-        dma4(dm.rs, dm.vs + i * dm.srow8 + (dm.sword ^ (8 * i)), 0, dm.ss + i * 8 * kSRow);
+        // rows of DMA i: (row >> 3) & 3 = skey ^ i (skey even when i < 2)
+        constexpr int i = D - kCodeDma;
+        dma4(dm.rs, dm.vs + i * dm.srow8 + (dm.sword ^ (8 * (dm.skey ^ i))), 0, dm.ss + i * 8 * kSRow);
     }
 }
 
@@ -229,17 +245,19 @@ __device__ __forceinline__ void issue_one(const Dma &dm) {
 __device__ __forceinline__ void issue_first(const Plan &pl, int wave) {
     const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(st0) + wave * 1024);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        dma16(pl.ra, pl.va + q * pl.row32, 0, st + q * 4096);
-        dma16(pl.rw, pl.vw + q * pl.row32, 0, st + kCodesA + q * 4096);
+    for (int q = 0; q < kCodeDma / 2; ++q) {
+        dma16(pl.ra, pl.va + q * pl.row32, 0, st + q * kWaves * 1024);
+        dma16(pl.rw, pl.vw + q * pl.row32, 0, st + kCodesA + q * kWaves * 1024);
     }
+    const int skey = (wave * (16 / kWaves)) & 3;
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
-        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_addr(sc0) + (part * 128 + wave * 32) * kSRow);
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_addr(sc0) +
+                                                           (part * 128 + wave * (128 / kWaves)) * kSRow);
         const uint32_t vs = (part < 2 ? pl.sa : pl.sw) + (uint32_t)(part & 1) * 16 * pl.srow8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dma4(part < 2 ? pl.rsa : pl.rsw, vs + i * pl.srow8 + (pl.sword ^ (8 * i)), 0,
+        for (int i = 0; i < kScaleDma; ++i)
+            dma4(part < 2 ? pl.rsa : pl.rsw, vs + i * pl.srow8 + (pl.sword ^ (8 * (skey ^ i))), 0,
                  ss + i * 8 * kSRow);
     }
 }
@@ -250,9 +268,9 @@ __device__ __forceinline__ i32x8 frag(const uint8_t *b, int row, int ch) {
 }
 
 // The fragments of one K step: rows wm*128 + j*32 + (lane % 32) of A and
-// wn*128 + i*32 + (lane % 32) of W, chunk 2 KS + kg.
+// wn*32*kTI + i*32 + (lane % 32) of W, chunk 2 KS + kg.
 struct Frags {
-    i32x8 a[4], w[4];
+    i32x8 a[4], w[kTI];
 };
 
 template <int KS>
@@ -262,25 +280,27 @@ __device__ __forceinline__ void load_frags(const uint8_t *__restrict__ b, int wm
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.a[j] = frag(b, wm * 128 + j * 32 + i32, ch);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.w[i] = frag(b + kCodesA, wn * 128 + i * 32 + i32, ch);
+    for (int i = 0; i < kTI; ++i) f.w[i] = frag(b + kCodesA, wn * 32 * kTI + i * 32 + i32, ch);
 }
 
-// The DMA issued after MFMA m of K step ks, or -1: the 16 code DMAs after
-// the odd MFMAs of steps 0 and 1, the 4 scale DMAs in step 2.  Spread out so
-// that the wave never waits long to hand a DMA over while its MFMAs could
-// issue; issued all at once after the barrier, they held the matrix cores
-// idle for a good part of every K tile.
+// The DMA issued after MFMA m of K step ks, or -1: the code DMAs after the
+// odd MFMAs of steps 0 and 1, the scale DMAs in step 2 after every fourth.
+// Spread out so that the wave never waits long to hand a DMA over while its
+// MFMAs could issue; issued all at once after the barrier, they held the
+// matrix cores idle for a good part of every K tile.
+constexpr int kNM = 4 * kTI;  // MFMAs per wave per K step
+static_assert(kCodeDma == kNM && kScaleDma * 4 == kNM, "the DMA slots of dma_after");
 constexpr int dma_after(int ks, int m) {
-    return ks < 2 ? ((m & 1) ? ks * 8 + (m >> 1) : -1)
-                  : (ks == 2 && (m & 3) == 3 ? 16 + (m >> 2) : -1);
+    return ks < 2 ? ((m & 1) ? ks * (kNM / 2) + (m >> 1) : -1)
+                  : (ks == 2 && (m & 3) == 3 ? kCodeDma + (m >> 2) : -1);
 }
 
 // MFMA m = 4 i + j of K step KS (its scale byte is byte 2 (KS % 2) of word
 // KS / 2, see compute), then its DMA if it has one; the scheduling barriers
 // keep the DMA where it is placed.
 template <int KS, int MI>
-__device__ __forceinline__ void mfma_one(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
-                                         f32x16 (&acc)[4][4], const Dma &dm) {
+__device__ __forceinline__ void mfma_one(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[kTI],
+                                         f32x16 (&acc)[kTI][4], const Dma &dm) {
     constexpr int kSel = 2 * (KS & 1), kWord = KS >> 1, i = MI >> 2, j = MI & 3;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         f.w[i], f.a[j], acc[i][j], 4, 4, kSel, (int)sw[i][kWord], kSel, (int)sa[j][kWord]);
@@ -293,17 +313,17 @@ __device__ __forceinline__ void mfma_one(const Frags &f, const u32x2 (&sa)[4], c
 }
 
 template <int KS, int... MI>
-__device__ __forceinline__ void mfma_seq(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
-                                         f32x16 (&acc)[4][4], const Dma &dm,
+__device__ __forceinline__ void mfma_seq(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[kTI],
+                                         f32x16 (&acc)[kTI][4], const Dma &dm,
                                          std::integer_sequence<int, MI...>) {
     (mfma_one<KS, MI>(f, sa, sw, acc, dm), ...);
 }
 
-// The 16 MFMAs of K step KS, with their share of the next K tile's DMAs.
+// The MFMAs of K step KS, with their share of the next K tile's DMAs.
 template <int KS>
-__device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[4],
-                                       f32x16 (&acc)[4][4], const Dma &dm) {
-    mfma_seq<KS>(f, sa, sw, acc, dm, std::make_integer_sequence<int, 16>{});
+__device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], const u32x2 (&sw)[kTI],
+                                       f32x16 (&acc)[kTI][4], const Dma &dm) {
+    mfma_seq<KS>(f, sa, sw, acc, dm, std::make_integer_sequence<int, kNM>{});
 }
 
 // The four K steps of stage b.  A row's 8 scale bytes (the stage's eight
@@ -315,14 +335,14 @@ __device__ __forceinline__ void mfma16(const Frags &f, const u32x2 (&sa)[4], con
 // the compiler read all four steps' fragments ahead and ran out of
 // registers).
 __device__ __forceinline__ void compute(const uint8_t *__restrict__ b, const uint8_t *__restrict__ sc,
-                                        int kq, int wm, int wn, int i32, int kg, f32x16 (&acc)[4][4],
+                                        int kq, int wm, int wn, int i32, int kg, f32x16 (&acc)[kTI][4],
                                         const Dma &dm) {
     // sc: the scale chunk; kq: the K tile within it.  Row r holds its four
     // K tiles' 8-byte groups at unit q ^ ((r >> 3) & 3) (so that 32
     // consecutive rows' reads of one K tile cover all banks); every row this
     // lane reads has (r >> 3) & 3 = (i32 >> 3) & 3.
     const int sx = 8 * (kq ^ ((i32 >> 3) & 3));
-    u32x2 sa[4], sw[4];
+    u32x2 sa[4], sw[kTI];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + i32;
@@ -330,8 +350,8 @@ __device__ __forceinline__ void compute(const uint8_t *__restrict__ b, const uin
         sa[j] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = kBM + wn * 128 + i * 32 + i32;
+    for (int i = 0; i < kTI; ++i) {
+        const int r = kBM + wn * 32 * kTI + i * 32 + i32;
         const uint64_t v = *reinterpret_cast<const uint64_t *>(sc + r * kSRow + sx) >> (8 * kg);
         sw[i] = u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
     }
@@ -362,7 +382,7 @@ __device__ __forceinline__ void tile_origin(int lin, int mtc, int ntc, int &m0, 
 // stage receives K tile kt + 1.
 template <int U>
 __device__ __forceinline__ void kstep(const Plan &pl, int kt, int KT, int wave, int wm, int wn,
-                                      int i32, int kg, f32x16 (&acc)[4][4]) {
+                                      int i32, int kg, f32x16 (&acc)[kTI][4]) {
     uint8_t *const rd = U == 0 ? st0 : st1;
     uint8_t *const in = U == 0 ? st1 : st0;
     // this wave's DMAs of tile kt have landed (none younger are in flight:
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
     const int tiles = mtc * ntc, per = (tiles + 7) / 8, wpx = gridDim.x >> 3;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWN, wn = wave % kWN;
     const int i32 = lane & 31, kg = lane >> 5;
     const int K2 = K / 2, K32 = K / 32, KT = K / kBK;
     for (int t = blockIdx.x >> 3; t < per; t += wpx) {
@@ -396,9 +416,9 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
         make_plan(pl, ac, as, wc, ws, m0, n0, M, N, K2, K32, wave, lane);
         issue_first(pl, wave);
 
-        f32x16 acc[4][4];
+        f32x16 acc[kTI][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
@@ -418,19 +438,18 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(
         KQW_WAIT_VM(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        const int ekey = kg ^ i32;
         // accumulator (i, j) register 4g + e of lane l: row wm*128 + j*32 + l%32,
-        // column wn*128 + i*32 + 8g + 4kg + e.  Stage s holds output rows
+        // column wn*32*kTI + i*32 + 8g + 4kg + e.  Stage s holds output rows
         // 128 s .. 128 s + 127, 512 bytes each, as 8-byte slots (col / 4) ^ (row & 31).
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint8_t *ob = (wm == 0 ? st0 : st1) + (j * 32 + i32) * 512 + 256 * wn;
+            uint8_t *ob = (wm == 0 ? st0 : st1) + (j * 32 + i32) * 512;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < kTI; ++i) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    // slot (wn*32 + i*8 + 2g + kg) ^ (row & 31), row & 31 = i32
-                    const int phys = (i * 8 + 2 * g) ^ ekey;
+                    // slot (wn*8*kTI + i*8 + 2g + kg) ^ (row & 31), row & 31 = i32
+                    const int phys = (wn * 8 * kTI + i * 8 + 2 * g + kg) ^ i32;
                     const uint32_t lo = acc_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
                     const uint32_t hi = acc_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                     *reinterpret_cast<u32x2 *>(ob + 8 * phys) = u32x2{lo, hi};

@@ -956,7 +956,9 @@ def test_gemm_full_size_sampled_rows(torch_cuda):
 # two such tiles per compute unit (a 4608 x 12288 output and larger) take it;
 # scales come in chunks of four K tiles of 256
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("M,N,K,pad", [(4100, 8200, 1280, 0),   # ragged tiles, 5 K tiles of 256
+@pytest.mark.parametrize("M,N,K,pad", [(4096, 8192, 768, 0),    # two full rounds on 256 CUs
+                                       (5100, 8192, 512, 8),    # last round half full
+                                       (4100, 8200, 1280, 0),   # ragged tiles, 5 K tiles of 256
                                        (4097, 8193, 256, 24),   # one K tile, strided output
                                        (4160, 8448, 512, 0),    # two K tiles
                                        (4352, 8192, 768, 8),    # three K tiles
