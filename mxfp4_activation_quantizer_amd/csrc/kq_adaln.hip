@@ -53,6 +53,7 @@ struct AdalnArgs {
     int64_t ldh;
     int64_t tokens;
     int d, nb, G, wps;           // row groups per workgroup, workgroups per sample
+    DivMagic nbm;                // division by nb
 };
 
 // Sum over the 64 lanes of a wave in the exchange order m = 1, 2, 4, 8, 16,
@@ -85,10 +86,11 @@ __device__ __forceinline__ float wave_total(float a) {
 // lanes needs (all 64 lanes take part; the loops are wave-uniform), so no
 // wave waits for another.
 template <int U>
-__device__ __forceinline__ void own_row_totals(const float *part, int nb, int G, int g, int nrows,
-                                               float (&tot)[U]) {
-    const int lane = threadIdx.x & 63, base = threadIdx.x & ~63;
-    const int g_lo = base / nb, g_top = (base + 63) / nb;
+__device__ __forceinline__ void own_row_totals(const float *part, int nb, DivMagic nbm, int G, int g,
+                                               int nrows, float (&tot)[U]) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+    const int g_lo = (int)udiv31(base, nbm), g_top = (int)udiv31(base + 63, nbm);
     const int g_hi = g_top < G - 1 ? g_top : G - 1;
 #pragma unroll
     for (int k = 0; k < U; ++k) tot[k] = 0.0f;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     const int nrows = rend - row0 < ROWS ? (int)(rend - row0) : ROWS;
 
     const int tid = threadIdx.x;
-    const int g = tid / nb, j = tid - g * nb;
+    const int g = (int)udiv31((uint32_t)tid, a.nbm), j = tid - g * nb;
     const bool act = g < a.G;
 
     // ---- parameters, then this thread's U units, then the sample vectors ----
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     }
     __syncthreads();
     float mu[U];
-    own_row_totals<U>(part, nb, a.G, g, nrows, mu);
+    own_row_totals<U>(part, nb, a.nbm, a.G, g, nrows, mu);
 
     // ---- pass 2: centered sums of squares -> 1/sqrt(var + eps) ----
 #pragma unroll
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(512) void adaln_kernel(AdalnArgs a) {
     }
     __syncthreads();
     float rs[U];
-    own_row_totals<U>(part2, nb, a.G, g, nrows, rs);
+    own_row_totals<U>(part2, nb, a.nbm, a.G, g, nrows, rs);
 #pragma unroll
     for (int k = 0; k < U; ++k) rs[k] = 1.0f / __builtin_sqrtf(rs[k] / (float)d + a.eps);
 
@@ -299,6 +301,7 @@ static kq_status launch_adaln(AdalnArgs a, void *stream) {
 template <bool QUANT>
 static kq_status run_adaln(AdalnArgs a, void *stream) {
     a.G = adaln_groups(a.nb);
+    a.nbm = div_magic((uint32_t)a.nb);
     switch (adaln_rows_per_thread()) {
         case 1: return launch_adaln<1, QUANT>(a, stream);
         case 4: return launch_adaln<4, QUANT>(a, stream);
