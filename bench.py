@@ -88,6 +88,7 @@ PROFILE_COMMANDS = """\
 cd /tmp && export TMPDIR=/tmp; cd $REPO
 python3 bench.py --json-out OUT/bench.json
 rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o trace -- python3 bench.py --steps 200 --warmup 50 --no-cpu
+rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_q -o trace_q -- python3 bench.py --kernel-only --steps 200 --warmup 50 --json-out OUT/trace_q.json
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o FETCH_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/WRITE_SIZE -o WRITE_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration --steps 20
@@ -259,6 +260,23 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                 lines.append(f"{entry:26s} {int(r['Calls']):6d} {avg:8.3f} "
                              f"{pct(r['Name'], 0.5):8.3f} {pct(r['Name'], 0.9):8.3f} "
                              f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} {rate}")
+    # the quantizer alone under the trace: its last `steps` dispatches are
+    # the timed region of that same process, whose own ms_per_step it printed
+    tq_path = os.path.join(out_dir, "trace_q.json")
+    if os.path.exists(tq_path):
+        with open(tq_path) as f:
+            tq = json.loads(f.readline())
+        rows = [r for r in _csv_rows(_find(os.path.join(out_dir, "trace_q"), "kernel_trace.csv"))
+                if _kmatch("kq_transform_quant", r["Kernel_Name"])]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        timed_rows = rows[-tq["steps"]:]
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed_rows]
+        avg = sum(dur) / len(dur)
+        lines += [f"# quantizer alone under the trace (OUT/trace_q, bench.py --kernel-only): its {len(dur)} "
+                  f"timed dispatches average {avg:.3f} us (median {sorted(dur)[len(dur) // 2]:.3f}) against "
+                  f"that process's own ms_per_step {tq['ms_per_step'] * 1e3:.3f} us "
+                  f"({avg / (tq['ms_per_step'] * 1e3):.3f} x); frac from the traced average "
+                  f"{nbytes / (avg * 1e3) / PEAK_HBM_GBS:.4f}"]
     bench_rec = None
     bench_path = os.path.join(out_dir, "bench.json")
     if os.path.exists(bench_path):
@@ -268,9 +286,9 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
                        if KERNEL_MATCH["kq_transform_quant"] in r["Name"]), float("nan"))
         bus = bench_rec["ms_per_step"] * 1e3
         lines += [f"# bench.py run in the same call (OUT/bench.json): ms_per_step {bus:.3f} us "
-                  f"({bench_rec['value']} GB/s, frac {bench_rec['roofline']['frac']}); traced "
-                  f"kq_transform_quant average {traced:.3f} us = {traced / bus:.3f} x ms_per_step; "
-                  f"frac from the traced average {nbytes / (traced * 1e3) / PEAK_HBM_GBS:.4f}"]
+                  f"({bench_rec['value']} GB/s, frac {bench_rec['roofline']['frac']}); the trace's "
+                  f"kq_transform_quant average over all its calls above (warm-up, peers, graph replays "
+                  f"and MALL-warm runs included) {traced:.3f} us = {traced / bus:.3f} x"]
     with open(os.path.join(PROFILES, f"kernel_stats_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     hc = (bench_rec or {}).get("peers", {}).get("hbm_ceiling")
@@ -752,7 +770,11 @@ def main() -> int:
             rec["GBps"] = gemm["weight_bytes"] / (ms * 1e-3) / 1e9
         else:
             rec["GBps"] = nbytes / (ms * 1e-3) / 1e9
+        rec["steps"] = args.steps
         print(json.dumps(rec), flush=True)
+        if args.json_out:
+            with open(args.json_out, "w") as f:
+                f.write(json.dumps(rec) + "\n")
         return 0
     ms = timed("kq_transform_quant", args.steps, args.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
