@@ -474,6 +474,56 @@ def graph_ms(torch, launch, n):
     return e0.elapsed_time(e1) / (3 * n)
 
 
+def other_workloads(L, torch, dev, sp, steps, warmup, names=("pixart", "flux_mlp")) -> dict:
+    """kq_transform_quant on the other activation shapes of the method's
+    configurations (PixArt-Sigma 8192 x 1152, FLUX-MLP 4608 x 12288), timed
+    like the value: seeded inputs of the workload's recipe, steps rotating
+    over buffer sets that together exceed twice the 256 MB MALL."""
+    import numpy as np
+    from mxfp4_activation_quantizer_amd import inputs, kq
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        T, d = w.tokens, w.d
+        nb = d // 32
+        nbytes = T * d * 2 + T * d // 2 + T * nb
+        R = max(2, -(-600_000_000 // nbytes))
+        x0 = torch.from_numpy(inputs.activation(name).view(np.int16)).to(dev)
+        xs = [x0] + [x0.clone() for _ in range(R - 1)]
+        lu = torch.from_numpy(inputs.lu_params(name).astype(np.float32)).to(dev)
+        codes = [torch.empty(T, d // 2, dtype=torch.uint8, device=dev) for _ in range(R)]
+        scales = [torch.empty(T, nb, dtype=torch.uint8, device=dev) for _ in range(R)]
+        args = [(xs[i].data_ptr(), T, d, d, lu.data_ptr(), codes[i].data_ptr(), scales[i].data_ptr(), sp)
+                for i in range(R)]
+        # untimed launches for 0.3 s (fresh buffers, clocks), then the warmup
+        t_end = time.perf_counter() + 0.3
+        i = 0
+        while time.perf_counter() < t_end or i < warmup:
+            st = L.kq_transform_quant(*args[i % R])
+            if st != 0:
+                raise kq.KQError("kq_transform_quant", st)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            L.kq_transform_quant(*args[i % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        g = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"config": f"{name}_{T}x{d}", "ms_per_step": round(ms, 6), "GBps": round(g, 1),
+                     "frac_of_hbm_peak": round(g / PEAK_HBM_GBS, 4),
+                     "tokens_per_s": round(T / (ms * 1e-3), 1), "rotating_buffer_sets": R}
+        del xs, x0, codes, scales, args
+        torch.cuda.empty_cache()
+    return out
+
+
 def hbm_ceilings(L, torch, dev, sp, xs, codes, scales, units, steps, warmup) -> dict:
     """What the memory system sustains for the quantizer's traffic, measured
     with kq_stream_ceiling (wave-contiguous loads and stores, no arithmetic, a
@@ -798,6 +848,8 @@ def main() -> int:
         extra["transform_quant_graph_replay"] = {
             "ms_per_step": round(gms, 6), "GBps": round(nbytes / (gms * 1e-3) / 1e9, 1),
             "note": "the same steps captured in one HIP graph and replayed; not the value"}
+        if args.workload == "flux_attn":
+            extra["other_workloads"] = other_workloads(L, torch, dev, sp, args.steps, args.warmup)
         extra["hbm_ceiling"] = hbm_ceilings(L, torch, dev, sp, xs, codes, scales, T * nb,
                                             args.steps, args.warmup)
         wms = timed_one_set("kq_transform_quant", args.steps, args.warmup)
