@@ -211,9 +211,13 @@ kq_status kq_dequant_inverse(const uint8_t *codes, const uint8_t *scales, int64_
  *
  * K % 128 == 0; M and N are arbitrary, with max(M, N) * K/2 < 2^31 (one
  * operand's codes under 2 GiB).  M == 0 or N == 0 returns KQ_OK.
- * With K % 512 == 0 and both scale arrays 16-byte aligned a faster kernel
- * runs (the K pipeline continues across output tiles); the results are the
- * same either way.
+ * One of three kernels runs, by shape and alignment: with K % 256 == 0 and
+ * at least two 256 x 256 output tiles per compute unit, 256 x 256 tiles;
+ * otherwise, with K % 512 == 0 and both scale arrays 16-byte aligned,
+ * 128 x 256 tiles with the K pipeline continuing across output tiles;
+ * otherwise 128 x 256 tiles one at a time.  All three accumulate every
+ * output over K in the same order (one MFMA per 64 K values, in K order), so
+ * the choice does not change the result.
  * KQ_ERR_HIP also if the library was built so that the kernel needs scratch
  * memory (its load waits count its own loads and would be wrong then).
  */
