@@ -992,3 +992,31 @@ def test_gemm_wide_tiles_random_mxfp4(torch_cuda, M, N, K, pad):
     assert_gemm_close(yb[rows, :N], Y, B, K)
     if ld > N:
         assert (inputs.bf16_bits_to_f32(yb[:, N:]) == -7.0).all()
+
+
+@pytest.mark.gpu
+def test_gemm_kernels_agree_bit_for_bit(torch_cuda):
+    # One 4608 x 12288 x 3072 call takes the 256 x 256-tile kernel.  The same
+    # rows computed by calls too small for it take the pipelined kernel
+    # (16-byte aligned scales) and the per-tile kernel (scales 4 bytes past a
+    # 16-byte boundary); every kernel accumulates each output over K in the
+    # same order, so all three must agree bit for bit.
+    torch = torch_cuda
+    M, N, K = 4608, 12288, 3072
+    g = np.random.default_rng(11)
+    ac, as_ = _random_mxfp4(g, M, K)
+    wc, ws = _random_mxfp4(g, N, K)
+    acd, asd, wcd, wsd = to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    kq.w4a4_gemm(acd, asd, wcd, wsd, y=y)
+    full = _np(y.view(torch.int16)).view(np.uint16)
+    for r0, rows, offset in ((0, 256, 0), (2048, 200, 0), (4400, 208, 4)):
+        sub_as = torch.empty(rows * (K // 32) + 16, dtype=torch.uint8, device="cuda:0")
+        sub_as = sub_as[offset:offset + rows * (K // 32)].view(rows, K // 32)
+        sub_as.copy_(asd[r0:r0 + rows])
+        ys = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda:0")
+        kq.w4a4_gemm(acd[r0:r0 + rows], sub_as, wcd, wsd, y=ys)
+        part = _np(ys.view(torch.int16)).view(np.uint16)
+        _log(f"GEMM rows {r0}..{r0 + rows - 1}, scales offset {offset}: "
+             f"{int((part != full[r0:r0 + rows]).sum())} outputs differ")
+        assert np.array_equal(part, full[r0:r0 + rows])
