@@ -1020,3 +1020,37 @@ def test_gemm_kernels_agree_bit_for_bit(torch_cuda):
         _log(f"GEMM rows {r0}..{r0 + rows - 1}, scales offset {offset}: "
              f"{int((part != full[r0:r0 + rows]).sum())} outputs differ")
         assert np.array_equal(part, full[r0:r0 + rows])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K,rows", [(96, 80, 512, None),        # 128 x 256-tile kernels
+                                        (4096, 8192, 512, (0, 17, 2049, 4095))])  # 256 x 256
+def test_gemm_wide_scale_range_and_nan_blocks(torch_cuda, M, N, K, rows):
+    # Scale bytes over a wide range (products from about 2^-124 to 2^120, no
+    # fp32 overflow), plus one activation block and one weight block whose
+    # scale byte is 0xFF: in the MX definition that block is NaN, so its
+    # whole output row (activation) or column (weight) is NaN, and no other
+    # output is.
+    torch = torch_cuda
+    g = np.random.default_rng(M + K)
+    ac, as_ = _random_mxfp4(g, M, K, 60, 181)
+    wc, ws = _random_mxfp4(g, N, K, 70, 181)
+    r_nan, c_nan = 17 % M, (N // 2 + 3) % N
+    as_[r_nan, 3] = 0xFF
+    ac[r_nan, 3 * 16:4 * 16] = 0
+    ws[c_nan, 0] = 0xFF
+    wc[c_nan, 0:16] = 0
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    kq.w4a4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(wc), to_gpu(ws), y=y)
+    yb = _np(y.view(torch.int16)).view(np.uint16)
+    sel = np.arange(M) if rows is None else np.unique(np.array(rows + (r_nan,)) % M)
+    Y, B = gemm_reference(ac[sel], as_[sel], wc, ws)
+    yf = inputs.bf16_bits_to_f32(yb[sel]).astype(np.float64)
+    nan_ref = np.isnan(Y)
+    assert nan_ref[sel == r_nan].all() and nan_ref[:, c_nan].all()
+    assert nan_ref.sum() == N * int((sel == r_nan).sum()) + len(sel) - int((sel == r_nan).sum())
+    np.testing.assert_array_equal(np.isnan(yf), nan_ref)
+    keep = np.arange(N) != c_nan
+    finite = sel != r_nan
+    assert_gemm_close(yb[sel][np.ix_(finite, keep)], Y[np.ix_(finite, keep)],
+                      B[np.ix_(finite, keep)], K)
