@@ -87,7 +87,7 @@ KERNEL_MATCH = {
 PROFILE_COMMANDS = """\
 cd /tmp && export TMPDIR=/tmp; cd $REPO
 python3 bench.py --json-out OUT/bench.json
-rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o trace -- python3 bench.py --steps 200 --warmup 50 --no-cpu
+rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o trace -- python3 bench.py --steps 200 --warmup 50 --no-cpu --no-other-workloads
 rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_q -o trace_q -- python3 bench.py --kernel-only --steps 200 --warmup 50 --json-out OUT/trace_q.json
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o FETCH_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/WRITE_SIZE -o WRITE_SIZE -- python3 bench.py --kernel-only --steps 20 --warmup 5
@@ -95,6 +95,8 @@ rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o copy_FE
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration --steps 20
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ -o SQ -- python3 bench.py --kernel-only --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_mfma -o SQ_mfma -- python3 bench.py --kernel-only --kernel kq_transform_quant_mfma --steps 20 --warmup 5
+rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_quad -o SQ_quad -- python3 bench.py --kernel-only --kernel kq_transform_quant_quad --steps 20 --warmup 5
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_quad -o FETCH_quad -- python3 bench.py --kernel-only --kernel kq_transform_quant_quad --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_gemm -o SQ_gemm -- python3 bench.py --kernel-only --kernel kq_w4a4_gemm --steps 20 --warmup 5
 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES --output-format csv -d OUT/SQ_adaln -o SQ_adaln -- python3 bench.py --kernel-only --kernel kq_adaln_transform_quant --steps 20 --warmup 5
 python3 bench.py --summarize-profiles OUT"""
@@ -372,6 +374,7 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
            f"# kernel sources {src_hash}; commands:"]
     ctr += ["#   " + c for c in profile_commands(workload)]
     for sub, entry in (("SQ", "kq_transform_quant"), ("SQ_mfma", "kq_transform_quant_mfma"),
+                       ("SQ_quad", "kq_transform_quant_quad"),
                        ("SQ_gemm", "kq_w4a4_gemm"), ("SQ_adaln", "kq_adaln_transform_quant")):
         if not any(f"OUT/{sub} " in c for c in profile_commands(workload)):
             continue  # no such pass for this workload
@@ -395,6 +398,11 @@ def summarize_profiles(out_dir: str, workload: str = "flux_attn") -> int:
         if entry == "kq_w4a4_gemm" and means.get("SQ_INSTS_MFMA"):
             ctr.append(f"  (one GEMM, {w.tokens}x{inputs.GEMM_N}x{inputs.GEMM_K}: "
                        f"{2 * w.tokens * inputs.GEMM_N * inputs.GEMM_K / means['SQ_INSTS_MFMA']:.0f} flops per MFMA instruction)")
+    if os.path.isdir(os.path.join(out_dir, "FETCH_quad")):
+        qf, nqf = counter_avg("FETCH_quad", "FETCH_SIZE", KERNEL_MATCH["kq_transform_quant_quad"])
+        ctr.append(f"kq_transform_quant_quad FETCH_SIZE per dispatch {qf:.1f} KiB (x{fs:.4f} copy scale) = "
+                   f"{qf * fs * 1024 / 1e6:.3f} MB read, against {read_b / 1e6:.3f} MB for "
+                   f"kq_transform_quant ({nqf} dispatches)")
     with open(os.path.join(PROFILES, f"counters_{workload}.txt"), "w") as f:
         f.write("\n".join(ctr) + "\n")
     print("\n".join(lines + txt + ctr))
@@ -609,6 +617,8 @@ def main() -> int:
     ap.add_argument("--workload", default="flux_attn",
                     choices=["pixart", "flux_attn", "flux_mlp"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the quantizer on the PixArt-Sigma and FLUX-MLP activations")
     ap.add_argument("--no-peers", action="store_true", help="skip the peer kernels")
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the timed steps of one kernel (for profilers)")
@@ -848,7 +858,7 @@ def main() -> int:
         extra["transform_quant_graph_replay"] = {
             "ms_per_step": round(gms, 6), "GBps": round(nbytes / (gms * 1e-3) / 1e9, 1),
             "note": "the same steps captured in one HIP graph and replayed; not the value"}
-        if args.workload == "flux_attn":
+        if args.workload == "flux_attn" and not args.no_other_workloads:
             extra["other_workloads"] = other_workloads(L, torch, dev, sp, args.steps, args.warmup)
         extra["hbm_ceiling"] = hbm_ceilings(L, torch, dev, sp, xs, codes, scales, T * nb,
                                             args.steps, args.warmup)
