@@ -55,6 +55,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; the entry points declared
+ * here are its only exported symbols. */
+#pragma GCC visibility push(default)
+
 typedef enum kq_status {
     KQ_OK = 0,
     KQ_ERR_NULL = 1,   /* a required pointer is NULL                         */
@@ -360,6 +364,8 @@ kq_status kq_copy_ceiling(const void *x, int64_t tokens, int64_t d, int64_t ld_x
  */
 kq_status kq_stream_ceiling(const void *src, int64_t units, uint8_t *codes, uint8_t *scales,
                             void *stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }
