@@ -28,6 +28,21 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
 
 
+def test_library_exports_nothing_but_the_declared_functions():
+    """Only the kq.h entry points are dynamic symbols: the host handles of the
+    kernels stay local, so a second build of the library in the same process
+    cannot take over this one's launches."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", kq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert names == set(kq.declared_functions()), sorted(names ^ set(kq.declared_functions()))[:10]
+
+
 def test_status_strings():
     assert kq.status_str(kq.KQ_OK) == "KQ_OK"
     for st in (kq.KQ_ERR_NULL, kq.KQ_ERR_SHAPE, kq.KQ_ERR_ALIGN, kq.KQ_ERR_HIP):
